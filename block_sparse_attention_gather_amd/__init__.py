@@ -1,0 +1,269 @@
+"""Python binding of libbsa: training-free block-sparse video attention on MI355X (gfx950).
+
+Argument marshalling only.  Every step runs in the HIP kernels of libbsa.so; PyTorch tensors
+supply device memory and the current HIP stream.  There is no fallback: if the library is not
+built, or a tensor is not on a GPU, the calls raise.
+
+    grid = Grid(T=21, H=30, W=52, tile=(4, 4, 8), block=128)
+    q_t = reorder(q, grid)                        # [b, N, h, D] -> [b, h, Npad, D]
+    row_ptr, col_idx, nnz = score_and_route(q_t, k_t, grid, top_p=0.9, k_floor=8)
+    out_t, lse = sparse_attn_fwd(q_t, k_t, v_t, row_ptr, col_idx, grid)
+    out = reorder(out_t, grid, inverse=True)      # [b, h, Npad, D] -> [b, N, h, D]
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbsa.so")
+
+BSA_OK = 0
+_STATUS = {-1: "BSA_ERR_INVALID_ARG", -2: "BSA_ERR_UNSUPPORTED", -3: "BSA_ERR_WORKSPACE",
+           -4: "BSA_ERR_HIP"}
+
+
+class BsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class _Grid(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("W", ctypes.c_int32),
+                ("tile_t", ctypes.c_int32), ("tile_h", ctypes.c_int32),
+                ("tile_w", ctypes.c_int32), ("block", ctypes.c_int32)]
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Grid:
+    """Latent grid T x H x W, 3D tile extent and block size (tokens per block)."""
+    T: int
+    H: int
+    W: int
+    tile: Tuple[int, int, int]
+    block: int
+
+    @property
+    def N(self) -> int:
+        return self.T * self.H * self.W
+
+    @property
+    def n_blk(self) -> int:
+        return -(-self.N // self.block)
+
+    @property
+    def Npad(self) -> int:
+        return self.n_blk * self.block
+
+    def _c(self) -> _Grid:
+        return _Grid(self.T, self.H, self.W, self.tile[0], self.tile[1], self.tile[2],
+                     self.block)
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libbsa.so not built at {LIB_PATH}; run "
+                          "`python -m block_sparse_attention_gather_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, F64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_double, ctypes.c_float,
+                            ctypes.c_size_t)
+    G, S = ctypes.POINTER(_Grid), ctypes.POINTER(_Shape)
+    sigs = {
+        "bsa_num_blocks": (I32, [G]),
+        "bsa_padded_len": (I32, [G]),
+        "bsa_reorder": (I32, [P, P, S, G, I32, P]),
+        "bsa_route_workspace_bytes": (SZ, [S, G]),
+        "bsa_score_and_route": (I32, [P, P, S, G, F64, I32, F64, P, P, P, P, P, SZ, P]),
+        "bsa_attn_workspace_bytes": (SZ, [S, G]),
+        "bsa_sparse_attn_fwd": (I32, [P, P, P, P, P, S, G, F32, P, P, P, SZ, P]),
+        "bsa_last_error": (ctypes.c_char_p, []),
+        "bsa_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def lib():
+    """The loaded ctypes library (raises if it is not built)."""
+    return _load()
+
+
+def version() -> str:
+    return _load().bsa_version().decode()
+
+
+def _check(status: int):
+    if status != BSA_OK:
+        raise BsaError(status, _load().bsa_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t) -> int:
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _require(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _shape(batch, heads, D) -> _Shape:
+    return _Shape(batch, heads, D)
+
+
+# ---------------------------------------------------------------------------------------
+def reorder(x, grid: Grid, inverse: bool = False, out=None):
+    """3D-tile token permutation.  inverse=False: raster [b, N, h, D] -> tiled [b, h, Npad, D]
+    (pad rows zero); inverse=True: tiled -> raster (pad rows dropped)."""
+    import torch
+    _require(x, torch.bfloat16, "x")
+    if not inverse:
+        b, N, h, D = x.shape
+        if N != grid.N:
+            raise ValueError(f"x has {N} tokens, grid has {grid.N}")
+        shape_out = (b, h, grid.Npad, D)
+    else:
+        b, h, Np, D = x.shape
+        if Np != grid.Npad:
+            raise ValueError(f"x has {Np} rows, grid pads to {grid.Npad}")
+        shape_out = (b, grid.N, h, D)
+    if out is None:
+        out = torch.empty(shape_out, dtype=x.dtype, device=x.device)
+    _require(out, torch.bfloat16, "out")
+    if tuple(out.shape) != shape_out:
+        raise ValueError(f"out must have shape {shape_out}")
+    g, s = grid._c(), _shape(b, h, D)
+    _check(_load().bsa_reorder(x.data_ptr(), out.data_ptr(), ctypes.byref(s), ctypes.byref(g),
+                               int(bool(inverse)), _stream(x)))
+    return out
+
+
+def route_workspace_bytes(batch, heads, D, grid: Grid) -> int:
+    g, s = grid._c(), _shape(batch, heads, D)
+    return int(_load().bsa_route_workspace_bytes(ctypes.byref(s), ctypes.byref(g)))
+
+
+def attn_workspace_bytes(batch, heads, D, grid: Grid) -> int:
+    g, s = grid._c(), _shape(batch, heads, D)
+    n = int(_load().bsa_attn_workspace_bytes(ctypes.byref(s), ctypes.byref(g)))
+    if n == 0:
+        _check(-4 if not _load().bsa_last_error() else -1)
+    return n
+
+
+def score_and_route(q_t, k_t, grid: Grid, top_p: float, k_floor: int,
+                    scale: Optional[float] = None, return_scores: bool = False,
+                    workspace=None, row_ptr=None, col_idx=None, nnz=None):
+    """Pooled block scores and Top-p / Top-k routing -> (row_ptr, col_idx, nnz[, scores]).
+
+    col_idx has the worst-case capacity rows * n_blk; its first nnz entries are the CSR
+    columns.  nnz stays on the device (a 1-element int32 tensor)."""
+    import torch
+    _require(q_t, torch.bfloat16, "q_t")
+    _require(k_t, torch.bfloat16, "k_t")
+    b, h, Np, D = q_t.shape
+    if tuple(k_t.shape) != (b, h, Np, D) or Np != grid.Npad:
+        raise ValueError("q_t/k_t must both be [b, h, Npad, D] for this grid")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dev = q_t.device
+    rows = b * h * grid.n_blk
+    if row_ptr is None:
+        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(rows * grid.n_blk, dtype=torch.int32, device=dev)
+    if nnz is None:
+        nnz = torch.empty(1, dtype=torch.int32, device=dev)
+    for t, n, size in ((row_ptr, "row_ptr", rows + 1), (col_idx, "col_idx", rows * grid.n_blk),
+                       (nnz, "nnz", 1)):
+        _require(t, torch.int32, n)
+        if t.numel() < size:
+            raise ValueError(f"{n} needs {size} int32 entries")
+    scores = (torch.empty((b, h, grid.n_blk, grid.n_blk), dtype=torch.float64, device=dev)
+              if return_scores else None)
+    need = route_workspace_bytes(b, h, D, grid)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    g, s = grid._c(), _shape(b, h, D)
+    _check(_load().bsa_score_and_route(
+        q_t.data_ptr(), k_t.data_ptr(), ctypes.byref(s), ctypes.byref(g), float(top_p),
+        int(k_floor), scale, row_ptr.data_ptr(), col_idx.data_ptr(), nnz.data_ptr(),
+        _ptr(scores), workspace.data_ptr(), workspace.numel(), _stream(q_t)))
+    if return_scores:
+        return row_ptr, col_idx, nnz, scores
+    return row_ptr, col_idx, nnz
+
+
+def sparse_attn_fwd(q_t, k_t, v_t, row_ptr, col_idx, grid: Grid,
+                    scale: Optional[float] = None, return_lse: bool = True, out=None,
+                    lse=None, workspace=None):
+    """Exact attention over the CSR-selected key blocks -> (out_t [b, h, Npad, D] bf16,
+    lse [b, h, Npad] fp32 or None)."""
+    import torch
+    for t, n in ((q_t, "q_t"), (k_t, "k_t"), (v_t, "v_t")):
+        _require(t, torch.bfloat16, n)
+    _require(row_ptr, torch.int32, "row_ptr")
+    _require(col_idx, torch.int32, "col_idx")
+    b, h, Np, D = q_t.shape
+    if tuple(k_t.shape) != (b, h, Np, D) or tuple(v_t.shape) != (b, h, Np, D):
+        raise ValueError("q_t/k_t/v_t must have the same shape")
+    if Np != grid.Npad:
+        raise ValueError(f"tiled tensors need {grid.Npad} rows")
+    if row_ptr.numel() != b * h * grid.n_blk + 1:
+        raise ValueError("row_ptr must have rows + 1 entries")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dev = q_t.device
+    if out is None:
+        out = torch.empty_like(q_t)
+    _require(out, torch.bfloat16, "out")
+    if return_lse and lse is None:
+        lse = torch.empty((b, h, Np), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(attn_workspace_bytes(b, h, D, grid), dtype=torch.uint8,
+                                device=dev)
+    g, s = grid._c(), _shape(b, h, D)
+    _check(_load().bsa_sparse_attn_fwd(
+        q_t.data_ptr(), k_t.data_ptr(), v_t.data_ptr(), row_ptr.data_ptr(), col_idx.data_ptr(),
+        ctypes.byref(s), ctypes.byref(g), scale, out.data_ptr(),
+        _ptr(lse) if return_lse else None, workspace.data_ptr(), workspace.numel(),
+        _stream(q_t)))
+    return out, (lse if return_lse else None)
+
+
+def layer(q, k, v, grid: Grid, top_p: float, k_floor: int, scale: Optional[float] = None):
+    """Whole path on raster [b, N, h, D] bf16 inputs -> (out [b, N, h, D], row_ptr, col_idx,
+    nnz)."""
+    q_t = reorder(q, grid)
+    k_t = reorder(k, grid)
+    v_t = reorder(v, grid)
+    row_ptr, col_idx, nnz = score_and_route(q_t, k_t, grid, top_p, k_floor, scale)
+    out_t, _ = sparse_attn_fwd(q_t, k_t, v_t, row_ptr, col_idx, grid, scale,
+                               return_lse=False)
+    return reorder(out_t, grid, inverse=True), row_ptr, col_idx, nnz

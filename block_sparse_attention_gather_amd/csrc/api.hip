@@ -1,0 +1,212 @@
+// C ABI of libbsa: argument validation, workspace sizing, per-device cache, error strings.
+// Every entry point validates on the host before enqueuing anything; no entry point
+// allocates device memory or synchronizes the stream.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <mutex>
+
+#include "bsa_internal.h"
+
+#define BSA_VERSION_STRING "libbsa 0.1.0 (gfx950)"
+
+namespace bsa {
+
+static thread_local char g_err[512] = "";
+
+bsa_status fail(bsa_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bsa_status check_launch(const char* what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(BSA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+    return BSA_OK;
+}
+
+// per-device properties, filled once per device ordinal
+static std::mutex g_dev_mu;
+static DeviceInfo g_dev[64];
+static bool g_dev_ok[64];
+
+bsa_status device_info(DeviceInfo* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(BSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(BSA_ERR_HIP, "device ordinal %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (!g_dev_ok[dev]) {
+        int cus = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess || cus <= 0)
+            return fail(BSA_ERR_HIP, "device %d CU count: %s", dev, hipGetErrorString(e));
+        g_dev[dev].device = dev;
+        g_dev[dev].cu_count = cus;
+        g_dev_ok[dev] = true;
+    }
+    *out = g_dev[dev];
+    return BSA_OK;
+}
+
+// ---- shared validation ------------------------------------------------------------------
+static bsa_status geometry(const bsa_grid* grid, Geometry* g) {
+    if (!grid) return fail(BSA_ERR_INVALID_ARG, "grid is NULL");
+    if (grid->T < 1 || grid->H < 1 || grid->W < 1)
+        return fail(BSA_ERR_INVALID_ARG, "grid T, H, W must be >= 1 (got %d, %d, %d)", grid->T,
+                    grid->H, grid->W);
+    if (grid->tile_t < 1 || grid->tile_h < 1 || grid->tile_w < 1)
+        return fail(BSA_ERR_INVALID_ARG, "tile extents must be >= 1");
+    if (grid->block < 1) return fail(BSA_ERR_INVALID_ARG, "block must be >= 1");
+    g->T = grid->T; g->H = grid->H; g->W = grid->W;
+    g->tt = grid->tile_t; g->th = grid->tile_h; g->tw = grid->tile_w;
+    g->B = grid->block;
+    g->N = (int64_t)grid->T * grid->H * grid->W;
+    if (g->N > ((int64_t)1 << 31) - 1) return fail(BSA_ERR_INVALID_ARG, "N = T*H*W exceeds int32");
+    const int64_t nb = (g->N + g->B - 1) / g->B;
+    g->n_blk = (int32_t)nb;
+    g->Npad = nb * g->B;
+    return BSA_OK;
+}
+
+static bsa_status check_shape(const bsa_shape* s) {
+    if (!s) return fail(BSA_ERR_INVALID_ARG, "shape is NULL");
+    if (s->batch < 1 || s->heads < 1 || s->head_dim < 1)
+        return fail(BSA_ERR_INVALID_ARG, "batch, heads, head_dim must be >= 1");
+    return BSA_OK;
+}
+
+static bsa_status check_kernel_dims(const bsa_shape* s, const Geometry& g) {
+    if (s->head_dim != 64 && s->head_dim != 128)
+        return fail(BSA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", s->head_dim);
+    if (g.B != 64 && g.B != 128)
+        return fail(BSA_ERR_UNSUPPORTED, "block %d unsupported (64 or 128)", g.B);
+    if ((int64_t)s->batch * s->heads > attn_max_heads())
+        return fail(BSA_ERR_UNSUPPORTED, "batch*heads %lld exceeds %d",
+                    (long long)s->batch * s->heads, attn_max_heads());
+    if (g.n_blk > attn_max_blocks())
+        return fail(BSA_ERR_UNSUPPORTED, "n_blk %d exceeds %d", g.n_blk, attn_max_blocks());
+    const int64_t rows = (int64_t)s->batch * s->heads * g.n_blk;
+    if (rows * g.n_blk > ((int64_t)1 << 31) - 1)
+        return fail(BSA_ERR_UNSUPPORTED, "rows*n_blk exceeds int32 CSR capacity");
+    if ((int64_t)s->batch * s->heads * g.Npad * s->head_dim > ((int64_t)1 << 40))
+        return fail(BSA_ERR_UNSUPPORTED, "tensor too large");
+    return BSA_OK;
+}
+
+}  // namespace bsa
+
+using namespace bsa;
+
+extern "C" {
+
+int32_t bsa_num_blocks(const bsa_grid* grid) {
+    Geometry g;
+    if (geometry(grid, &g) != BSA_OK) return 0;
+    return g.n_blk;
+}
+
+int32_t bsa_padded_len(const bsa_grid* grid) {
+    Geometry g;
+    if (geometry(grid, &g) != BSA_OK) return 0;
+    return g.Npad > INT32_MAX ? 0 : (int32_t)g.Npad;
+}
+
+bsa_status bsa_reorder(const void* src, void* dst, const bsa_shape* shape, const bsa_grid* grid,
+                       int32_t inverse, void* stream) {
+    Geometry g;
+    bsa_status st = geometry(grid, &g);
+    if (st != BSA_OK) return st;
+    if ((st = check_shape(shape)) != BSA_OK) return st;
+    if (!src || !dst) return fail(BSA_ERR_INVALID_ARG, "src/dst is NULL");
+    if (shape->head_dim % 8 != 0 || shape->head_dim > 1024)
+        return fail(BSA_ERR_UNSUPPORTED, "reorder head_dim must be a multiple of 8 in [8, 1024]");
+    if (((uintptr_t)src | (uintptr_t)dst) & 15)
+        return fail(BSA_ERR_INVALID_ARG, "src/dst must be 16-byte aligned");
+    const int64_t elems_src = (int64_t)shape->batch * shape->heads * (inverse ? g.Npad : g.N) *
+                              shape->head_dim * 2;
+    const int64_t elems_dst = (int64_t)shape->batch * shape->heads * (inverse ? g.N : g.Npad) *
+                              shape->head_dim * 2;
+    const char* s0 = (const char*)src;
+    const char* d0 = (const char*)dst;
+    if (s0 < d0 + elems_dst && d0 < s0 + elems_src)
+        return fail(BSA_ERR_INVALID_ARG, "src and dst overlap");
+    return launch_reorder(src, dst, shape->batch, shape->heads, shape->head_dim, g, inverse,
+                          (hipStream_t)stream);
+}
+
+size_t bsa_route_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid) {
+    Geometry g;
+    if (geometry(grid, &g) != BSA_OK || check_shape(shape) != BSA_OK) return 0;
+    return route_ws_bytes(shape->batch, shape->heads, shape->head_dim, g);
+}
+
+bsa_status bsa_score_and_route(const void* q_t, const void* k_t, const bsa_shape* shape,
+                               const bsa_grid* grid, double top_p, int32_t k_floor,
+                               double scale, int32_t* row_ptr, int32_t* col_idx, int32_t* nnz,
+                               double* block_scores, void* ws, size_t ws_bytes, void* stream) {
+    Geometry g;
+    bsa_status st = geometry(grid, &g);
+    if (st != BSA_OK) return st;
+    if ((st = check_shape(shape)) != BSA_OK) return st;
+    if (!q_t || !k_t || !row_ptr || !col_idx || !nnz)
+        return fail(BSA_ERR_INVALID_ARG, "q_t, k_t, row_ptr, col_idx and nnz must be non-NULL");
+    if (!(top_p >= 0.0 && top_p <= 1.0))
+        return fail(BSA_ERR_INVALID_ARG, "top_p must lie in [0, 1] (got %g)", top_p);
+    if (k_floor < 1) return fail(BSA_ERR_INVALID_ARG, "k_floor must be >= 1 (got %d)", k_floor);
+    if (!isfinite(scale)) return fail(BSA_ERR_INVALID_ARG, "scale must be finite");
+    if ((st = check_kernel_dims(shape, g)) != BSA_OK) return st;
+    if ((((uintptr_t)q_t | (uintptr_t)k_t) & 15))
+        return fail(BSA_ERR_INVALID_ARG, "q_t/k_t must be 16-byte aligned");
+    const size_t need = route_ws_bytes(shape->batch, shape->heads, shape->head_dim, g);
+    if (!ws || ws_bytes < need || ((uintptr_t)ws & 255))
+        return fail(BSA_ERR_WORKSPACE, "route workspace: need %zu bytes, 256-byte aligned", need);
+    return launch_route(q_t, k_t, shape->batch, shape->heads, shape->head_dim, g, top_p, k_floor,
+                        scale, row_ptr, col_idx, nnz, block_scores, ws, (hipStream_t)stream);
+}
+
+size_t bsa_attn_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid) {
+    Geometry g;
+    if (geometry(grid, &g) != BSA_OK || check_shape(shape) != BSA_OK) return 0;
+    if (check_kernel_dims(shape, g) != BSA_OK) return 0;
+    DeviceInfo dev;
+    if (device_info(&dev) != BSA_OK) return 0;
+    return attn_ws_bytes(shape->batch, shape->heads, shape->head_dim, g,
+                         attn_slots(shape->head_dim, g.B, dev));
+}
+
+bsa_status bsa_sparse_attn_fwd(const void* q_t, const void* k_t, const void* v_t,
+                               const int32_t* row_ptr, const int32_t* col_idx,
+                               const bsa_shape* shape, const bsa_grid* grid, float scale,
+                               void* out_t, float* lse, void* ws, size_t ws_bytes,
+                               void* stream) {
+    Geometry g;
+    bsa_status st = geometry(grid, &g);
+    if (st != BSA_OK) return st;
+    if ((st = check_shape(shape)) != BSA_OK) return st;
+    if (!q_t || !k_t || !v_t || !row_ptr || !col_idx || !out_t)
+        return fail(BSA_ERR_INVALID_ARG, "q_t, k_t, v_t, row_ptr, col_idx, out_t must be non-NULL");
+    if (!isfinite(scale)) return fail(BSA_ERR_INVALID_ARG, "scale must be finite");
+    if ((st = check_kernel_dims(shape, g)) != BSA_OK) return st;
+    if ((((uintptr_t)q_t | (uintptr_t)k_t | (uintptr_t)v_t | (uintptr_t)out_t) & 15))
+        return fail(BSA_ERR_INVALID_ARG, "q_t/k_t/v_t/out_t must be 16-byte aligned");
+    DeviceInfo dev;
+    if ((st = device_info(&dev)) != BSA_OK) return st;
+    const size_t need = attn_ws_bytes(shape->batch, shape->heads, shape->head_dim, g,
+                                      attn_slots(shape->head_dim, g.B, dev));
+    if (!ws || ws_bytes < need || ((uintptr_t)ws & 255))
+        return fail(BSA_ERR_WORKSPACE, "attention workspace: need %zu bytes, 256-byte aligned",
+                    need);
+    return launch_attn(q_t, k_t, v_t, row_ptr, col_idx, shape->batch, shape->heads,
+                       shape->head_dim, g, scale, out_t, lse, ws, dev, (hipStream_t)stream);
+}
+
+const char* bsa_last_error(void) { return g_err; }
+
+const char* bsa_version(void) { return BSA_VERSION_STRING; }
+
+}  // extern "C"

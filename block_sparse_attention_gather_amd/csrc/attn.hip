@@ -1,0 +1,594 @@
+// Exact block-sparse attention forward over CSR key-block lists, bf16 MFMA on gfx950.
+//
+// What is computed (FVAttn page, abstract: attention over the materialized block mask; PSA
+// page, "Approach": one block-sparse kernel; VC-Attention abstract: the running row maximum
+// and row sum of an online softmax): for each real query of block i, softmax attention over
+// the real keys of the blocks listed for row (b, h, i), evaluated block by block with an
+// online softmax (running max m, running sum l, rescaled accumulator).
+//
+// Scheduling (FVAttn page, abstract: adaptive Top-p gives uneven per-head work; its runtime
+// load balancing moves heavy heads between GPUs - here the same problem is solved between the
+// compute units of one GPU):
+//   plan_global  one workgroup: chunk size Kc from nnz, per-head work, heads assigned to the
+//                8 XCD queues longest-first (each head's K/V then stays in one XCD's L2),
+//                queue offsets, counters reset.
+//   plan_rows    one workgroup per head: rows ordered by cost descending (ties: row order),
+//                rows longer than Kc split into chunks, work items written in queue order.
+//   attn         persistent: each workgroup reads its XCD id, pops items from its own queue
+//                with an atomic counter, then steals from the other queues; every queue is
+//                visited once after it runs dry, so every workgroup exits.  A split row's
+//                chunks store unnormalised partials; the chunk that finishes last merges them
+//                in chunk order, so results do not depend on timing.
+//
+// Data layout of one work item (B = 128, D = 128; B = D = 64 analogous): 4 wavefronts, each
+// owning 32 query rows.  S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T in
+// registers) leaves each lane one query and 16 keys per 32x32 tile, so the row max is one
+// cross-half exchange and the row sum stays per lane until the end.  P^T is already the B
+// operand layout of O^T = V^T P^T; V is stored transposed in LDS with its keys permuted
+// inside every 16-key group to match, and both LDS tiles have rows padded by 16 bytes so the
+// 32 lanes of a half-wave read distinct banks.
+#include "bsa_internal.h"
+
+namespace bsa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kNQ = 8;             // XCD queues (MI355X: 8 XCDs)
+constexpr int kPlanThreads = 1024;
+constexpr int kMaxHeads = 2048;    // batch * heads supported by the planner
+constexpr int kMaxBlocks = 4096;   // n_blk supported by the planner
+constexpr int kKcMin = 8;          // smallest chunk (blocks) a row is split into
+constexpr float kRescaleThresh = 8.0f;   // log2 units the running max may lag
+
+struct AttnLayout {
+    size_t hdr, head_item_off, head_slot_base, items, done, part_o, part_ml, total;
+    int64_t max_items, max_slots;
+};
+
+// header ints: [0] Kc, [16 + 32 q] queue counters (128 B apart), [8 .. 8+kNQ) qstart,
+// [272 ..) qlen
+constexpr int kHdrKc = 0;
+constexpr int kHdrQStart = 8;
+constexpr int kHdrCtr = 32;         // + 32*q
+constexpr int kHdrQLen = 32 + 32 * kNQ;
+constexpr int kHdrInts = kHdrQLen + kNQ;
+
+AttnLayout attn_layout(int32_t batch, int32_t heads, int32_t D, const Geometry& g,
+                       int slots) {
+    AttnLayout L;
+    const int64_t bh = (int64_t)batch * heads;
+    const int64_t rows = bh * g.n_blk;
+    const int64_t target = 2 * (int64_t)slots;
+    L.max_items = rows + target;
+    L.max_slots = 2 * target;
+    size_t off = 0;
+    L.hdr = off;            off = align_up(off + kHdrInts * 4, 256);
+    L.head_item_off = off;  off = align_up(off + bh * 4, 256);
+    L.head_slot_base = off; off = align_up(off + bh * 4, 256);
+    L.items = off;          off = align_up(off + L.max_items * 16, 256);
+    L.done = off;           off = align_up(off + L.max_slots * 4, 256);
+    L.part_o = off;         off = align_up(off + (size_t)L.max_slots * g.B * D * 4, 256);
+    L.part_ml = off;        off = align_up(off + (size_t)L.max_slots * g.B * 2 * 4, 256);
+    L.total = off;
+    return L;
+}
+
+// ---------------------------------------------------------------------------------------
+// planner
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(kPlanThreads) void plan_global_kernel(
+    const int32_t* __restrict__ row_ptr, int32_t n_blk, int32_t nbh, int32_t target,
+    int32_t* __restrict__ hdr, int32_t* __restrict__ head_item_off,
+    int32_t* __restrict__ head_slot_base) {
+    __shared__ int32_t hitems[kMaxHeads], hslots[kMaxHeads], hrank[kMaxHeads];
+    __shared__ int32_t horder[kMaxHeads], hqueue[kMaxHeads];
+    __shared__ int64_t qload[kNQ];
+    __shared__ int32_t qlen[kNQ], qstart[kNQ], qrun[kNQ];
+    const int t = threadIdx.x;
+    const int64_t rows = (int64_t)nbh * n_blk;
+    const int64_t total = row_ptr[rows];
+    int64_t kc64 = (total + target - 1) / target;
+    const int32_t Kc = (int32_t)(kc64 < kKcMin ? kKcMin : kc64);
+    for (int h = t; h < nbh; h += kPlanThreads) { hitems[h] = 0; hslots[h] = 0; }
+    __syncthreads();
+    for (int64_t r = t; r < rows; r += kPlanThreads) {
+        const int32_t c = row_ptr[r + 1] - row_ptr[r];
+        int32_t ni = (c + Kc - 1) / Kc;
+        ni = ni < 1 ? 1 : ni;
+        const int h = (int)(r / n_blk);
+        atomicAdd(&hitems[h], ni);
+        if (ni > 1) atomicAdd(&hslots[h], ni);
+    }
+    // heads ranked by cost (kept blocks) descending, ties by index
+    for (int h = t; h < nbh; h += kPlanThreads) {
+        const int32_t ch = row_ptr[(int64_t)(h + 1) * n_blk] - row_ptr[(int64_t)h * n_blk];
+        int rk = 0;
+        for (int h2 = 0; h2 < nbh; ++h2) {
+            const int32_t c2 = row_ptr[(int64_t)(h2 + 1) * n_blk] - row_ptr[(int64_t)h2 * n_blk];
+            rk += (c2 > ch) || (c2 == ch && h2 < h);
+        }
+        hrank[h] = rk;
+        horder[rk] = h;
+    }
+    __syncthreads();
+    if (t == 0) {
+        for (int q = 0; q < kNQ; ++q) { qload[q] = 0; qlen[q] = 0; qrun[q] = 0; }
+        // longest-processing-time-first: each head to the least-loaded queue
+        for (int k = 0; k < nbh; ++k) {
+            const int h = horder[k];
+            int best = 0;
+            for (int q = 1; q < kNQ; ++q)
+                if (qload[q] < qload[best]) best = q;
+            qload[best] += row_ptr[(int64_t)(h + 1) * n_blk] - row_ptr[(int64_t)h * n_blk];
+            qlen[best] += hitems[h];
+            hqueue[h] = best;
+        }
+        int32_t acc = 0;
+        for (int q = 0; q < kNQ; ++q) { qstart[q] = acc; acc += qlen[q]; }
+        for (int k = 0; k < nbh; ++k) {
+            const int h = horder[k];
+            const int q = hqueue[h];
+            head_item_off[h] = qstart[q] + qrun[q];
+            qrun[q] += hitems[h];
+        }
+        int32_t sacc = 0;
+        for (int h = 0; h < nbh; ++h) { head_slot_base[h] = sacc; sacc += hslots[h]; }
+        hdr[kHdrKc] = Kc;
+        for (int q = 0; q < kNQ; ++q) {
+            hdr[kHdrQStart + q] = qstart[q];
+            hdr[kHdrQLen + q] = qlen[q];
+            hdr[kHdrCtr + 32 * q] = 0;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_rows_kernel(
+    const int32_t* __restrict__ row_ptr, int32_t n_blk, const int32_t* __restrict__ hdr,
+    const int32_t* __restrict__ head_item_off, const int32_t* __restrict__ head_slot_base,
+    int4* __restrict__ items, int32_t* __restrict__ done) {
+    __shared__ int32_t cost[kMaxBlocks], ord[kMaxBlocks], ipos[kMaxBlocks], spos[kMaxBlocks];
+    __shared__ int32_t part_i[kPlanThreads], part_s[kPlanThreads];
+    const int t = threadIdx.x;
+    const int h = blockIdx.x;
+    const int64_t base = (int64_t)h * n_blk;
+    const int32_t Kc = hdr[kHdrKc];
+    for (int i = t; i < n_blk; i += kPlanThreads) cost[i] = row_ptr[base + i + 1] - row_ptr[base + i];
+    __syncthreads();
+    for (int i = t; i < n_blk; i += kPlanThreads) {
+        const int32_t ci = cost[i];
+        int rk = 0;
+        for (int i2 = 0; i2 < n_blk; ++i2) {
+            const int32_t c2 = cost[i2];
+            rk += (c2 > ci) || (c2 == ci && i2 < i);
+        }
+        ord[rk] = i;
+    }
+    __syncthreads();
+    // exclusive scans (in rank order) of items per row and of partial slots per split row
+    const int seg = (n_blk + kPlanThreads - 1) / kPlanThreads;
+    const int lo = min(n_blk, t * seg), hi = min(n_blk, lo + seg);
+    int32_t li = 0, ls = 0;
+    for (int k = lo; k < hi; ++k) {
+        int32_t ni = (cost[ord[k]] + Kc - 1) / Kc;
+        ni = ni < 1 ? 1 : ni;
+        li += ni;
+        ls += ni > 1 ? ni : 0;
+    }
+    part_i[t] = li;
+    part_s[t] = ls;
+    __syncthreads();
+    for (int off = 1; off < kPlanThreads; off <<= 1) {
+        const int32_t ai = t >= off ? part_i[t - off] : 0;
+        const int32_t as = t >= off ? part_s[t - off] : 0;
+        __syncthreads();
+        part_i[t] += ai;
+        part_s[t] += as;
+        __syncthreads();
+    }
+    int32_t ri = part_i[t] - li, rs = part_s[t] - ls;
+    for (int k = lo; k < hi; ++k) {
+        int32_t ni = (cost[ord[k]] + Kc - 1) / Kc;
+        ni = ni < 1 ? 1 : ni;
+        ipos[k] = ri;
+        spos[k] = rs;
+        ri += ni;
+        rs += ni > 1 ? ni : 0;
+    }
+    __syncthreads();
+    const int32_t ioff = head_item_off[h];
+    const int32_t sbase = head_slot_base[h];
+    for (int k = t; k < n_blk; k += kPlanThreads) {
+        const int i = ord[k];
+        const int32_t c = cost[i];
+        const int32_t beg = row_ptr[base + i];
+        int32_t ni = (c + Kc - 1) / Kc;
+        ni = ni < 1 ? 1 : ni;
+        const int32_t slot = ni > 1 ? sbase + spos[k] : -1;
+        for (int s = 0; s < ni; ++s) {
+            const int32_t b0 = beg + s * Kc;
+            const int32_t b1 = min(beg + (s + 1) * Kc, beg + c);
+            items[ioff + ipos[k] + s] = make_int4((int32_t)(base + i), b0, b1, slot);
+        }
+        if (slot >= 0) done[slot] = 0;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// attention
+// ---------------------------------------------------------------------------------------
+struct AttnArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* row_ptr;
+    const int32_t* col_idx;
+    uint16_t* out;
+    float* lse;
+    const int32_t* hdr;
+    int32_t* ctr;           // queue counters (hdr + kHdrCtr), 32 ints apart
+    const int4* items;
+    int32_t* done;
+    float* part_o;
+    float* part_ml;
+    int64_t N, Npad;
+    int32_t n_blk;
+    float scale_log2;       // softmax scale * log2(e)
+};
+
+__device__ __forceinline__ int xcc_id() {
+    // HW_REG_XCC_ID (hwreg 20), bits [3:0]
+    return (int)(__builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) & 0xf);
+}
+
+__device__ __forceinline__ uint16_t f2bf(float x) {
+    const __bf16 b = (__bf16)x;
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+// key slot inside the transposed V tile: swap bits 2 and 3 of the key offset in its
+// 16-key group, so a half-wave's 8 keys of one MFMA k-step are contiguous
+__device__ __forceinline__ int vslot(int key) {
+    return (key & ~15) | (key & 3) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+
+template <int D, int B>
+struct Tile {
+    static constexpr int NW = B / 32;          // wavefronts per workgroup
+    static constexpr int NT = NW * 64;         // threads
+    static constexpr int KCH = D / 8;          // 16-byte chunks in a K row
+    static constexpr int VCH = B / 8;          // 16-byte chunks in a V^T row
+    static constexpr int NKT = B / 32;         // key tiles of S^T
+    static constexpr int NKK = D / 16;         // MFMA k-steps of S^T
+    static constexpr int NDT = D / 32;         // d tiles of O^T
+    static constexpr int NPK = B / 16;         // MFMA k-steps of O^T
+    static constexpr int LOADS = B * KCH / NT; // 16-byte chunks per thread per tile
+};
+
+// Cooperative load of key block `blk` of head `bh` into LDS.  Both tiles use rows padded by
+// one 16-byte chunk (K: [B][D + 8], V^T: [D][B + 8]), so 32 consecutive rows read at the same
+// column hit distinct bank groups and every address is a per-lane base plus a constant.  V is
+// written transposed, two keys packed per 32-bit store, at the permuted key slots.  Rows at
+// or past N are zero.
+template <int D, int B>
+__device__ __forceinline__ void load_kv(const AttnArgs& a, int64_t bh, int32_t blk,
+                                       uint16_t* Ks, uint16_t* Vt) {
+    using Tl = Tile<D, B>;
+    constexpr int KP = D + 8, VP = B + 8;
+    constexpr int PAIRS = Tl::LOADS / 2;   // key pairs per thread
+    const int t = threadIdx.x;
+    const int64_t row0 = (int64_t)blk * B;
+    const uint4* kg = (const uint4*)(a.k + (bh * a.Npad + row0) * D);
+    const uint4* vg = (const uint4*)(a.v + (bh * a.Npad + row0) * D);
+    const int64_t nreal = a.N - row0;
+#pragma unroll
+    for (int u = 0; u < PAIRS; ++u) {
+        const int c = t + Tl::NT * u;            // pair-chunk index
+        const int key = 2 * (c / Tl::KCH);       // even key of the pair
+        const int ch = c % Tl::KCH;
+        const bool ok0 = key < nreal, ok1 = key + 1 < nreal;
+        const uint4 k0 = ok0 ? kg[key * Tl::KCH + ch] : make_uint4(0, 0, 0, 0);
+        const uint4 k1 = ok1 ? kg[(key + 1) * Tl::KCH + ch] : make_uint4(0, 0, 0, 0);
+        const uint4 v0 = ok0 ? vg[key * Tl::KCH + ch] : make_uint4(0, 0, 0, 0);
+        const uint4 v1 = ok1 ? vg[(key + 1) * Tl::KCH + ch] : make_uint4(0, 0, 0, 0);
+        *(uint4*)(Ks + key * KP + ch * 8) = k0;
+        *(uint4*)(Ks + (key + 1) * KP + ch * 8) = k1;
+        uint32_t* vt = (uint32_t*)(Vt + (ch * 8) * VP + vslot(key));
+        const uint32_t a0[4] = {v0.x, v0.y, v0.z, v0.w};
+        const uint32_t a1[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // d = 8 ch + 2e: low halves; d + 1: high halves
+            vt[(2 * e) * (VP / 2)] = __builtin_amdgcn_perm(a1[e], a0[e], 0x05040100u);
+            vt[(2 * e + 1) * (VP / 2)] = __builtin_amdgcn_perm(a1[e], a0[e], 0x07060302u);
+        }
+    }
+}
+
+// Merge the unnormalised partials (O_s, m_s, l_s) of a split row in chunk order:
+// O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
+template <int D, int B>
+__device__ __noinline__ void combine_split(const AttnArgs& a, int64_t bh, int32_t iblk,
+                                           int32_t slot0, int32_t nchunk) {
+    constexpr int NT = Tile<D, B>::NT;
+    for (int idx = threadIdx.x; idx < B * D; idx += NT) {
+        const int qq = idx / D, d = idx % D;
+        const int64_t qp = (int64_t)iblk * B + qq;
+        float M = -INFINITY;
+        for (int c = 0; c < nchunk; ++c)
+            M = fmaxf(M, a.part_ml[((int64_t)(slot0 + c) * B + qq) * 2]);
+        float num = 0.f, den = 0.f;
+        for (int c = 0; c < nchunk; ++c) {
+            const int64_t sl = slot0 + c;
+            const float w = __builtin_amdgcn_exp2f(a.part_ml[(sl * B + qq) * 2] - M);
+            num = fmaf(w, a.part_o[(sl * B + qq) * D + d], num);
+            den = fmaf(w, a.part_ml[(sl * B + qq) * 2 + 1], den);
+        }
+        const bool real = qp < a.N;
+        a.out[(bh * a.Npad + qp) * D + d] = (real && den > 0.f) ? f2bf(num / den) : (uint16_t)0;
+        if (d == 0 && a.lse)
+            a.lse[bh * a.Npad + qp] =
+                (real && den > 0.f) ? (M + __log2f(den)) * 0.69314718055994531f : 0.f;
+    }
+}
+
+template <int D, int B>
+__global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
+    using Tl = Tile<D, B>;
+    __shared__ __align__(16) uint16_t Ks[B * (D + 8)];
+    __shared__ __align__(16) uint16_t Vt[D * (B + 8)];
+    __shared__ int s_pop;
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wv = t >> 6;
+    const int half = lane >> 5;      // 0 / 1
+    const int l32 = lane & 31;
+    const int q0 = xcc_id() % kNQ;
+    const int32_t Kc = a.hdr[kHdrKc];
+
+    for (int qo = 0; qo < kNQ; ++qo) {
+        const int qi = (q0 + qo) % kNQ;
+        const int32_t qlen = a.hdr[kHdrQLen + qi];
+        const int32_t qstart = a.hdr[kHdrQStart + qi];
+        while (true) {
+            if (t == 0) s_pop = atomicAdd(&a.ctr[32 * qi], 1);
+            __syncthreads();
+            const int32_t pop = s_pop;
+            __syncthreads();
+            if (pop >= qlen) break;
+            const int4 it = a.items[qstart + pop];
+            const int64_t row = it.x;
+            const int64_t bh = row / a.n_blk;
+            const int32_t iblk = (int32_t)(row - bh * a.n_blk);
+            const int64_t qrow0 = (int64_t)iblk * B + wv * 32;   // first query row of wave
+
+            // Q^T operand: lane holds query l32, d = 16 kk + 8 half .. +8
+            bf16x8 qf[Tl::NKK];
+            {
+                const int64_t qpos = qrow0 + l32;
+                const uint16_t* qp = a.q + (bh * a.Npad + qpos) * D + 8 * half;
+#pragma unroll
+                for (int kk = 0; kk < Tl::NKK; ++kk) {
+                    uint4 raw = qpos < a.N ? *(const uint4*)(qp + 16 * kk) : make_uint4(0, 0, 0, 0);
+                    qf[kk] = __builtin_bit_cast(bf16x8, raw);
+                }
+            }
+            f32x16 o[Tl::NDT];
+#pragma unroll
+            for (int dt = 0; dt < Tl::NDT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+            float m = -INFINITY, l = 0.f;
+
+            for (int32_t e = it.y; e < it.z; ++e) {
+                const int32_t blk = a.col_idx[e];
+                __syncthreads();                       // previous tile fully consumed
+                load_kv<D, B>(a, bh, blk, Ks, Vt);
+                __syncthreads();
+                // S^T = K Q^T
+                f32x16 s[Tl::NKT];
+#pragma unroll
+                for (int tt = 0; tt < Tl::NKT; ++tt) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s[tt][r] = 0.f;
+                    const int key = 32 * tt + l32;
+#pragma unroll
+                    for (int kk = 0; kk < Tl::NKK; ++kk) {
+                        const bf16x8 kf =
+                            *(const bf16x8*)(Ks + key * (D + 8) + (2 * kk + half) * 8);
+                        s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[tt], 0, 0, 0);
+                    }
+                }
+                // pad keys of a short last block
+                if (a.N - (int64_t)blk * B < B) {
+                    const int lim = (int)(a.N - (int64_t)blk * B) - 4 * half;
+#pragma unroll
+                    for (int tt = 0; tt < Tl::NKT; ++tt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            if (32 * tt + 8 * (r >> 2) + (r & 3) >= lim) s[tt][r] = -INFINITY;
+                }
+                // online softmax (log2 domain, lazy rescale)
+                float mx = -INFINITY;
+#pragma unroll
+                for (int tt = 0; tt < Tl::NKT; ++tt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tt][r]);
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                const float mnew = mx * a.scale_log2;
+                if (__any(mnew > m + kRescaleThresh)) {
+                    const float mn = fmaxf(m, mnew);
+                    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+                    l *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < Tl::NDT; ++dt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+                    m = mn;
+                }
+                bf16x8 pf[Tl::NPK];
+#pragma unroll
+                for (int tt = 0; tt < Tl::NKT; ++tt)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                        for (int e8 = 0; e8 < 8; ++e8) {
+                            const float p = __builtin_amdgcn_exp2f(
+                                fmaf(s[tt][8 * hh + e8], a.scale_log2, -m));
+                            l += p;
+                            pf[2 * tt + hh][e8] = (__bf16)p;
+                        }
+                // O^T += V^T P^T
+#pragma unroll
+                for (int dt = 0; dt < Tl::NDT; ++dt) {
+                    const int d = 32 * dt + l32;
+#pragma unroll
+                    for (int ks = 0; ks < Tl::NPK; ++ks) {
+                        const bf16x8 vf =
+                            *(const bf16x8*)(Vt + d * (B + 8) + (2 * ks + half) * 8);
+                        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[dt], 0, 0, 0);
+                    }
+                }
+            }
+
+            const float lt = l + __shfl_xor(l, 32, 64);
+            const int64_t qpos = qrow0 + l32;
+            if (it.w < 0) {
+                // whole row in this item: normalise and store
+                const float inv = lt > 0.f ? 1.f / lt : 0.f;
+                const bool real = qpos < a.N;
+                uint16_t* op = a.out + (bh * a.Npad + qpos) * D;
+#pragma unroll
+                for (int dt = 0; dt < Tl::NDT; ++dt)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int d = 32 * dt + 8 * g4 + 4 * half;
+                        ushort4 pk;
+                        pk.x = real ? f2bf(o[dt][4 * g4 + 0] * inv) : 0;
+                        pk.y = real ? f2bf(o[dt][4 * g4 + 1] * inv) : 0;
+                        pk.z = real ? f2bf(o[dt][4 * g4 + 2] * inv) : 0;
+                        pk.w = real ? f2bf(o[dt][4 * g4 + 3] * inv) : 0;
+                        *(ushort4*)(op + d) = pk;
+                    }
+                if (a.lse && half == 0)
+                    a.lse[bh * a.Npad + qpos] =
+                        (real && lt > 0.f) ? (m + __log2f(lt)) * 0.69314718055994531f : 0.f;
+            } else {
+                // one chunk of a split row: store the unnormalised partial
+                const int32_t rbeg = a.row_ptr[row];
+                const int32_t cnt = a.row_ptr[row + 1] - rbeg;
+                const int32_t chunk = (it.y - rbeg) / Kc;
+                const int32_t nchunk = (cnt + Kc - 1) / Kc;
+                const int64_t slot = it.w + chunk;
+                float* po = a.part_o + (slot * B + wv * 32 + l32) * D;
+#pragma unroll
+                for (int dt = 0; dt < Tl::NDT; ++dt)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int d = 32 * dt + 8 * g4 + 4 * half;
+                        *(float4*)(po + d) = make_float4(o[dt][4 * g4], o[dt][4 * g4 + 1],
+                                                         o[dt][4 * g4 + 2], o[dt][4 * g4 + 3]);
+                    }
+                if (half == 0) {
+                    a.part_ml[(slot * B + wv * 32 + l32) * 2 + 0] = m;
+                    a.part_ml[(slot * B + wv * 32 + l32) * 2 + 1] = lt;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                __syncthreads();
+                if (t == 0) s_pop = atomicAdd(&a.done[it.w], 1);
+                __syncthreads();
+                const int32_t prev = s_pop;
+                __syncthreads();
+                if (prev == nchunk - 1) {
+                    // last chunk to finish: merge all partials in chunk order
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                    combine_split<D, B>(a, bh, iblk, it.w, nchunk);
+                }
+            }
+        }
+    }
+}
+
+template <int D, int B>
+bsa_status run(const AttnArgs& a, int slots, hipStream_t s) {
+    hipLaunchKernelGGL((attn_kernel<D, B>), dim3(slots), dim3(Tile<D, B>::NT), 0, s, a);
+    return check_launch("sparse_attn");
+}
+
+template <int D, int B>
+int occupancy() {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_kernel<D, B>, Tile<D, B>::NT, 0) !=
+        hipSuccess)
+        return 1;
+    return nb < 1 ? 1 : nb;
+}
+
+}  // namespace
+
+int attn_slots(int32_t D, int32_t B, const DeviceInfo& dev) {
+    int occ;
+    if (D == 128 && B == 128) occ = occupancy<128, 128>();
+    else if (D == 64 && B == 64) occ = occupancy<64, 64>();
+    else if (D == 128 && B == 64) occ = occupancy<128, 64>();
+    else occ = occupancy<64, 128>();
+    return dev.cu_count * occ;
+}
+
+size_t attn_ws_bytes(int32_t batch, int32_t heads, int32_t D, const Geometry& g, int slots) {
+    return attn_layout(batch, heads, D, g, slots).total;
+}
+
+bsa_status launch_attn(const void* q_t, const void* k_t, const void* v_t,
+                       const int32_t* row_ptr, const int32_t* col_idx, int32_t batch,
+                       int32_t heads, int32_t D, const Geometry& g, float scale, void* out_t,
+                       float* lse, void* ws, const DeviceInfo& dev, hipStream_t s) {
+    const int slots = attn_slots(D, g.B, dev);
+    const AttnLayout L = attn_layout(batch, heads, D, g, slots);
+    unsigned char* w = (unsigned char*)ws;
+    int32_t* hdr = (int32_t*)(w + L.hdr);
+    int32_t* head_item_off = (int32_t*)(w + L.head_item_off);
+    int32_t* head_slot_base = (int32_t*)(w + L.head_slot_base);
+    int4* items = (int4*)(w + L.items);
+    int32_t* done = (int32_t*)(w + L.done);
+    const int32_t nbh = batch * heads;
+
+    hipLaunchKernelGGL(plan_global_kernel, dim3(1), dim3(kPlanThreads), 0, s, row_ptr, g.n_blk,
+                       nbh, 2 * slots, hdr, head_item_off, head_slot_base);
+    bsa_status st = check_launch("plan_global");
+    if (st != BSA_OK) return st;
+    hipLaunchKernelGGL(plan_rows_kernel, dim3(nbh), dim3(kPlanThreads), 0, s, row_ptr, g.n_blk,
+                       hdr, head_item_off, head_slot_base, items, done);
+    st = check_launch("plan_rows");
+    if (st != BSA_OK) return st;
+
+    AttnArgs a;
+    a.q = (const uint16_t*)q_t;
+    a.k = (const uint16_t*)k_t;
+    a.v = (const uint16_t*)v_t;
+    a.row_ptr = row_ptr;
+    a.col_idx = col_idx;
+    a.out = (uint16_t*)out_t;
+    a.lse = lse;
+    a.hdr = hdr;
+    a.ctr = hdr + kHdrCtr;
+    a.items = items;
+    a.done = done;
+    a.part_o = (float*)(w + L.part_o);
+    a.part_ml = (float*)(w + L.part_ml);
+    a.N = g.N;
+    a.Npad = g.Npad;
+    a.n_blk = g.n_blk;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    if (D == 128 && g.B == 128) return run<128, 128>(a, slots, s);
+    if (D == 64 && g.B == 64) return run<64, 64>(a, slots, s);
+    if (D == 128 && g.B == 64) return run<128, 64>(a, slots, s);
+    return run<64, 128>(a, slots, s);
+}
+
+int attn_max_heads() { return kMaxHeads; }
+int attn_max_blocks() { return kMaxBlocks; }
+
+}  // namespace bsa

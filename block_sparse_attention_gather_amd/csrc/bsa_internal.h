@@ -1,0 +1,54 @@
+// Internal declarations shared by the libbsa translation units (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/bsa.h"
+
+namespace bsa {
+
+// ---- geometry ----------------------------------------------------------------------
+struct Geometry {
+    int32_t T, H, W, tt, th, tw, B;
+    int64_t N;        // real tokens
+    int32_t n_blk;    // ceil(N / B)
+    int64_t Npad;     // n_blk * B
+};
+
+// ---- error reporting (thread-local message, see bsa_last_error) ---------------------
+bsa_status fail(bsa_status st, const char* fmt, ...);
+bsa_status check_launch(const char* what);
+
+// ---- per-device properties (read once per device, then cached) ---------------------
+struct DeviceInfo {
+    int device;           // HIP device ordinal
+    int cu_count;         // compute units
+};
+bsa_status device_info(DeviceInfo* out);
+// persistent attention workgroups for one device: CUs x resident workgroups per CU
+int attn_slots(int32_t D, int32_t B, const DeviceInfo& dev);
+int attn_max_heads();
+int attn_max_blocks();
+
+// ---- launchers (defined next to their kernels) -------------------------------------
+bsa_status launch_reorder(const void* src, void* dst, int32_t batch, int32_t heads,
+                          int32_t D, const Geometry& g, int inverse, hipStream_t s);
+
+size_t route_ws_bytes(int32_t batch, int32_t heads, int32_t D, const Geometry& g);
+bsa_status launch_route(const void* q_t, const void* k_t, int32_t batch, int32_t heads,
+                        int32_t D, const Geometry& g, double top_p, int32_t k_floor,
+                        double scale, int32_t* row_ptr, int32_t* col_idx, int32_t* nnz,
+                        double* block_scores, void* ws, hipStream_t s);
+
+size_t attn_ws_bytes(int32_t batch, int32_t heads, int32_t D, const Geometry& g, int slots);
+bsa_status launch_attn(const void* q_t, const void* k_t, const void* v_t,
+                       const int32_t* row_ptr, const int32_t* col_idx, int32_t batch,
+                       int32_t heads, int32_t D, const Geometry& g, float scale, void* out_t,
+                       float* lse, void* ws, const DeviceInfo& dev, hipStream_t s);
+
+// ---- small helpers -------------------------------------------------------------------
+static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace bsa

@@ -1,0 +1,140 @@
+/*
+ * bsa.h - C ABI of libbsa, training-free block-sparse self-attention for video diffusion
+ * transformers on AMD Instinct MI355X (gfx950).
+ *
+ * The method (FVAttn page, abstract): a sparse-routing frontend made of video-aware block
+ * organization, Top-p routing and a Top-k safety floor materializes a block mask; attention
+ * then runs exactly over the kept blocks with an online softmax (the row maximum and row sum
+ * that an online softmax keeps: VC-Attention page, abstract; block-sparse kernels: PSA page,
+ * "Approach", DFSAttn abstract).  The library splits this into three calls:
+ *
+ *   bsa_reorder          token permutation into 3D tiles (and its inverse)
+ *   bsa_score_and_route  per-block mean pooling, pooled block scores, Top-p/Top-k -> CSR
+ *   bsa_sparse_attn_fwd  exact block-sparse attention over the CSR lists
+ *
+ * Conventions shared by every call
+ *   - Tensor arguments are DEVICE pointers (HIP device memory of the current device).  The
+ *     caller allocates and owns every buffer, workspaces included; the library never
+ *     allocates device memory and keeps no state between calls apart from a read-only
+ *     per-device property cache.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns; no call synchronizes the host or reads device data.
+ *   - bf16 is IEEE bfloat16 (uint16 storage).  Results are written with round-to-nearest-even.
+ *   - Arguments are validated on the host before anything is enqueued.  A non-OK status
+ *     means nothing was enqueued (except BSA_ERR_HIP, returned when a launch itself fails);
+ *     bsa_last_error() then returns a message for the calling thread.
+ *   - Calls are thread-safe.  Calls that write the same buffers must not overlap.
+ *
+ * Token layout
+ *   raster   [batch, N, heads, D]      token n = (t*H + h)*W + w of the T x H x W latent grid
+ *   tiled    [batch, heads, Npad, D]   tile order; n_blk = ceil(N / block), Npad = n_blk*block;
+ *                                      positions N..Npad-1 are padding (zero after reorder)
+ *   Rows of the routing are (batch, head, query block) triples, numbered
+ *   r = (b*heads + h)*n_blk + i.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BSA_OK = 0,
+    BSA_ERR_INVALID_ARG = -1,   /* null pointer, non-positive size, p outside [0,1], ...   */
+    BSA_ERR_UNSUPPORTED = -2,   /* head_dim or block size the kernels are not built for     */
+    BSA_ERR_WORKSPACE = -3,     /* workspace pointer NULL or smaller than the query returns */
+    BSA_ERR_HIP = -4            /* a HIP launch or device query failed                      */
+} bsa_status;
+
+/* Latent grid and block organization.  Tiles are visited in (it, ih, iw) order, the last tile
+ * along an axis is truncated to what is left of the grid, and tokens inside a tile are
+ * row-major (t, h, w).  Blocks are `block` consecutive tokens of that order.  The tile volume
+ * need not equal `block` (a block may then straddle tiles). */
+typedef struct {
+    int32_t T, H, W;                  /* latent grid, N = T*H*W real tokens            */
+    int32_t tile_t, tile_h, tile_w;   /* 3D tile extent, each >= 1                     */
+    int32_t block;                    /* tokens per block: 64 or 128                   */
+} bsa_grid;
+
+typedef struct {
+    int32_t batch, heads, head_dim;   /* head_dim: 64 or 128                           */
+} bsa_shape;
+
+/* ---- host-only helpers ------------------------------------------------------------- */
+/* ceil(N / block) and n_blk * block; 0 for an invalid grid. */
+int32_t bsa_num_blocks(const bsa_grid* grid);
+int32_t bsa_padded_len(const bsa_grid* grid);
+
+/* ---- 1. video-aware block organization (FVAttn abstract) --------------------------- */
+/* inverse == 0: src raster bf16 [batch, N, heads, D] -> dst tiled bf16 [batch, heads, Npad, D];
+ *               dst pad rows (positions >= N) are written with zeros.
+ * inverse != 0: src tiled [batch, heads, Npad, D] -> dst raster [batch, N, heads, D]; pad rows
+ *               of src are not read.
+ * src and dst must not overlap.  Supported head_dim: any multiple of 8 in [8, 1024]. */
+bsa_status bsa_reorder(const void* src, void* dst, const bsa_shape* shape,
+                       const bsa_grid* grid, int32_t inverse, void* stream);
+
+/* ---- 2. routing frontend: pooled block scores, Top-p with a Top-k floor (FVAttn) ---- */
+/* Workspace bytes bsa_score_and_route needs (depends on shape and grid only). */
+size_t bsa_route_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid);
+
+/* For every row (b, h, i):
+ *   qbar_i, kbar_j = means of the tiled Q and K over the real tokens of block i / j (fp64),
+ *   s_ij = scale * <qbar_i, kbar_j>  (fp64),  mass_ij = softmax_j(s_ij) over all n_blk blocks,
+ *   order j by s_ij descending (equal scores: smaller j first), keep the shortest prefix
+ *   whose cumulative mass reaches top_p (top_p >= 1: all; top_p == 0: none; all if rounding
+ *   never reaches top_p), then raise the count to min(n_blk, k_floor).
+ * Outputs, CSR over rows:
+ *   row_ptr [rows + 1] int32, row_ptr[0] = 0;
+ *   col_idx capacity rows*n_blk int32 (worst case), kept key blocks of each row ascending;
+ *   nnz     [1] int32 = row_ptr[rows];
+ *   block_scores (optional, may be NULL) [batch, heads, n_blk, n_blk] fp64 s_ij.
+ * q_t, k_t: tiled bf16 [batch, heads, Npad, D] (pad rows are ignored).
+ * Errors: top_p NaN or outside [0, 1], k_floor < 1, scale not finite -> BSA_ERR_INVALID_ARG;
+ * rows*n_blk must fit int32; n_blk <= 4096.
+ * ws: device workspace of at least bsa_route_workspace_bytes() bytes, 256-byte aligned. */
+bsa_status bsa_score_and_route(const void* q_t, const void* k_t, const bsa_shape* shape,
+                               const bsa_grid* grid, double top_p, int32_t k_floor,
+                               double scale, int32_t* row_ptr, int32_t* col_idx,
+                               int32_t* nnz, double* block_scores, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* ---- 3. exact block-sparse attention (online softmax over the kept blocks) --------- */
+/* Workspace bytes bsa_sparse_attn_fwd needs: worst case over every possible CSR, so the host
+ * never needs nnz. */
+size_t bsa_attn_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid);
+
+/* For every real query position p of block i in row r = (b, h, i):
+ *   U = real key positions of the blocks col_idx[row_ptr[r] .. row_ptr[r+1]),
+ *   logit_pu = scale * <Q_p, K_u>  (bf16 inputs, fp32 accumulation),
+ *   out_t[p] = sum_u softmax_u(logit_pu) V_u  (bf16),  lse[p] = log sum_u exp(logit_pu) (fp32).
+ * Pad query rows (p >= N) of out_t and lse are written with zeros.
+ * q_t, k_t, v_t, out_t: tiled bf16 [batch, heads, Npad, D]; lse: [batch, heads, Npad] fp32 or
+ * NULL.  Every row must keep at least one block; col_idx values must lie in [0, n_blk) and be
+ * distinct within a row (bsa_score_and_route guarantees both; other CSRs are the caller's
+ * responsibility and are not checked on the device).
+ * The heavy-row scheduler is persistent: work items are built on the device from the CSR row
+ * lengths, long rows are split and their partial results merged in a fixed order, so the
+ * output is bitwise deterministic.
+ * ws: device workspace of at least bsa_attn_workspace_bytes() bytes, 256-byte aligned. */
+bsa_status bsa_sparse_attn_fwd(const void* q_t, const void* k_t, const void* v_t,
+                               const int32_t* row_ptr, const int32_t* col_idx,
+                               const bsa_shape* shape, const bsa_grid* grid, float scale,
+                               void* out_t, float* lse, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* ---- diagnostics ------------------------------------------------------------------- */
+/* Message of the calling thread's last non-OK status ("" if none).  Valid until the next
+ * call on the same thread. */
+const char* bsa_last_error(void);
+const char* bsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H */

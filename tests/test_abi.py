@@ -1,0 +1,144 @@
+"""The C ABI without a GPU: header hygiene, exported symbols, host-side validation."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_attention_gather_amd as bsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsa_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_compiles_as_c99_and_cxx(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "bsa.h"\nint main(void){bsa_grid g={1,1,1,1,1,1,64};'
+                   'return bsa_num_blocks(&g) == 1 ? 0 : 1;}\n')
+    for cc, extra in (("gcc", ["-std=c99"]), ("g++", ["-std=c++11", "-x", "c++"])):
+        r = subprocess.run([cc, *extra, "-Wall", "-Werror", "-pedantic", "-fsyntax-only",
+                            "-I", os.path.dirname(HEADER), str(src)],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) == 9, names
+    lib = ctypes.CDLL(bsa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    r = subprocess.run(["nm", "-D", "--defined-only", bsa.LIB_PATH], capture_output=True,
+                       text=True)
+    exported = set(re.findall(r"\bT (bsa_\w+)", r.stdout))
+    assert set(names) <= exported
+    assert exported <= set(names), exported - set(names)     # nothing undeclared leaks
+
+
+def test_version_and_geometry_helpers():
+    assert "gfx950" in bsa.version()
+    L = bsa.lib()
+    for (T, H, W, tile, B), (nb, npad) in [((2, 16, 16, (4, 4, 4), 64), (8, 512)),
+                                            ((21, 30, 52, (4, 4, 8), 128), (256, 32768)),
+                                            ((33, 45, 80, (4, 4, 8), 128), (929, 118912)),
+                                            ((1, 1, 1, (4, 4, 8), 128), (1, 128))]:
+        g = bsa.Grid(T, H, W, tile, B)._c()
+        assert L.bsa_num_blocks(ctypes.byref(g)) == nb
+        assert L.bsa_padded_len(ctypes.byref(g)) == npad
+    bad = bsa.Grid(0, 16, 16, (4, 4, 4), 64)._c()
+    assert L.bsa_num_blocks(ctypes.byref(bad)) == 0
+
+
+FAKE = 0x7f0000000000            # never dereferenced: validation fails before any launch
+
+
+def _route(**kw):
+    L = bsa.lib()
+    g = kw.pop("grid", bsa.Grid(2, 16, 16, (4, 4, 4), 64))._c()
+    s = bsa._Shape(*kw.pop("shape", (1, 2, 64)))
+    args = dict(q=FAKE, k=FAKE, top_p=0.9, k_floor=2, scale=0.125, row_ptr=FAKE, col=FAKE,
+                nnz=FAKE, scores=None, ws=FAKE, ws_bytes=1 << 30)
+    args.update(kw)
+    st = L.bsa_score_and_route(args["q"], args["k"], ctypes.byref(s), ctypes.byref(g),
+                               args["top_p"], args["k_floor"], args["scale"], args["row_ptr"],
+                               args["col"], args["nnz"], args["scores"], args["ws"],
+                               args["ws_bytes"], None)
+    return st, L.bsa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(q=None), -1, "non-NULL"),
+    (dict(nnz=None), -1, "non-NULL"),
+    (dict(top_p=1.5), -1, "top_p"),
+    (dict(top_p=-0.1), -1, "top_p"),
+    (dict(top_p=float("nan")), -1, "top_p"),
+    (dict(k_floor=0), -1, "k_floor"),
+    (dict(scale=float("inf")), -1, "scale"),
+    (dict(shape=(1, 2, 96)), -2, "head_dim"),
+    (dict(grid=bsa.Grid(2, 16, 16, (4, 4, 4), 32)), -2, "block"),
+    (dict(shape=(1, 3000, 64)), -2, "batch*heads"),
+    (dict(ws=None), -3, "workspace"),
+    (dict(ws_bytes=16), -3, "workspace"),
+    (dict(ws=FAKE + 8), -3, "aligned"),
+    (dict(q=FAKE + 2), -1, "aligned"),
+    (dict(grid=bsa.Grid(2, 0, 16, (4, 4, 4), 64)), -1, "grid"),
+])
+def test_route_validation(kw, status, msg):
+    st, err = _route(**kw)
+    assert st == status, (st, err)
+    assert msg in err
+
+
+def test_reorder_validation():
+    L = bsa.lib()
+    g = bsa.Grid(2, 16, 16, (4, 4, 4), 64)._c()
+    s = bsa._Shape(1, 2, 64)
+    assert L.bsa_reorder(None, FAKE, ctypes.byref(s), ctypes.byref(g), 0, None) == -1
+    s_bad = bsa._Shape(1, 2, 12)
+    assert L.bsa_reorder(FAKE, FAKE + (1 << 24), ctypes.byref(s_bad), ctypes.byref(g), 0,
+                         None) == -2
+    # overlapping buffers
+    assert L.bsa_reorder(FAKE, FAKE + 64, ctypes.byref(s), ctypes.byref(g), 0, None) == -1
+    assert "overlap" in L.bsa_last_error().decode()
+    assert L.bsa_reorder(FAKE, FAKE, None, ctypes.byref(g), 0, None) == -1
+
+
+def test_attn_validation_before_device_query():
+    L = bsa.lib()
+    g = bsa.Grid(2, 16, 16, (4, 4, 4), 64)._c()
+    s = bsa._Shape(1, 2, 64)
+    st = L.bsa_sparse_attn_fwd(FAKE, FAKE, None, FAKE, FAKE, ctypes.byref(s), ctypes.byref(g),
+                               0.125, FAKE, None, FAKE, 1 << 30, None)
+    assert st == -1
+    s96 = bsa._Shape(1, 2, 96)
+    st = L.bsa_sparse_attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s96),
+                               ctypes.byref(g), 0.125, FAKE, None, FAKE, 1 << 30, None)
+    assert st == -2
+    st = L.bsa_sparse_attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s), ctypes.byref(g),
+                               float("nan"), FAKE, None, FAKE, 1 << 30, None)
+    assert st == -1
+
+
+def test_route_workspace_size_is_host_computable():
+    L = bsa.lib()
+    for cfg, D in (((21, 30, 52, (4, 4, 8), 128), 128), ((2, 16, 16, (4, 4, 4), 64), 64)):
+        g = bsa.Grid(*cfg)._c()
+        s = bsa._Shape(1, 40, D)
+        n = L.bsa_route_workspace_bytes(ctypes.byref(s), ctypes.byref(g))
+        nb = L.bsa_num_blocks(ctypes.byref(g))
+        assert n >= 2 * 40 * nb * D * 8          # pooled Q and K in fp64
+        assert n % 256 == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((1, 512, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        bsa.reorder(x, bsa.Grid(2, 16, 16, (4, 4, 4), 64))
