@@ -247,69 +247,95 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
     return __builtin_bit_cast(uint16_t, b);
 }
 
-// key slot inside the transposed V tile: swap bits 2 and 3 of the key offset in its
-// 16-key group, so a half-wave's 8 keys of one MFMA k-step are contiguous
-__device__ __forceinline__ int vslot(int key) {
-    return (key & ~15) | (key & 3) | ((key & 4) << 1) | ((key & 8) >> 1);
+// Read-only int32 data of the scheduler (CSR columns, work items, header) read through the
+// constant address space: uniform indices then compile to scalar loads, which do not share
+// the vector-memory counter with the LDS DMA.
+typedef __attribute__((address_space(4))) const int32_t cint32;
+__device__ __forceinline__ int32_t ld_const(const int32_t* p, int64_t i) {
+    return ((cint32*)p)[i];
+}
+__device__ __forceinline__ int4 ld_const4(const int4* p, int64_t i) {
+    const int32_t* q = (const int32_t*)p + 4 * i;
+    return make_int4(ld_const(q, 0), ld_const(q, 1), ld_const(q, 2), ld_const(q, 3));
 }
 
 template <int D, int B>
 struct Tile {
     static constexpr int NW = B / 32;          // wavefronts per workgroup
     static constexpr int NT = NW * 64;         // threads
-    static constexpr int KCH = D / 8;          // 16-byte chunks in a K row
-    static constexpr int VCH = B / 8;          // 16-byte chunks in a V^T row
+    static constexpr int KCH = D / 8;          // 16-byte chunks in a K or V row
     static constexpr int NKT = B / 32;         // key tiles of S^T
     static constexpr int NKK = D / 16;         // MFMA k-steps of S^T
     static constexpr int NDT = D / 32;         // d tiles of O^T
     static constexpr int NPK = B / 16;         // MFMA k-steps of O^T
-    static constexpr int LOADS = B * KCH / NT; // 16-byte chunks per thread per tile
+    static constexpr int TI = B * KCH / (NW * 64);   // LDS-DMA instructions per wave per tile
 };
 
-// Cooperative load of key block `blk` of head `bh` into LDS.  Both tiles use rows padded by
-// one 16-byte chunk (K: [B][D + 8], V^T: [D][B + 8]), so 32 consecutive rows read at the same
-// column hit distinct bank groups and every address is a per-lane base plus a constant.  V is
-// written transposed, two keys packed per 32-bit store, at the permuted key slots.  Rows at
-// or past N are zero.
-template <int D, int B>
-__device__ __forceinline__ void load_kv(const AttnArgs& a, int64_t bh, int32_t blk,
-                                       uint16_t* Ks, uint16_t* Vt) {
+// 16-byte-chunk swizzles of the row-major K and V tiles in LDS (row r, logical chunk c is
+// stored at chunk c ^ swz(r) of row r):
+//  K: the 32 lanes of a half-wave read rows r..r+31 at one chunk (ds_read_b128), so
+//     swz(r) = r mod chunks puts any 8 consecutive rows on 8 distinct bank groups;
+//  V: a 16-lane group of ds_read_b64_tr_b16 reads 4 consecutive rows x 2 adjacent chunks,
+//     so swz(r) = 2r mod chunks keeps those 8 chunks on 8 distinct bank groups.
+template <int KCH> __device__ __forceinline__ int swz_k(int r) { return r & (KCH - 1); }
+template <int KCH> __device__ __forceinline__ int swz_v(int r) { return (2 * r) & (KCH - 1); }
+
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    // s_waitcnt vmcnt(n) with expcnt / lgkmcnt left unconstrained (gfx9 encoding)
+    if (n == 0) __builtin_amdgcn_s_waitcnt(0x0f70);
+    else if (n == 4) __builtin_amdgcn_s_waitcnt(0x0f74);
+    else if (n == 8) __builtin_amdgcn_s_waitcnt(0x0f78);
+    else __builtin_amdgcn_s_waitcnt(0x0f70);
+}
+
+// Workgroup barrier that also orders this wave's LDS reads (ds_read results consumed) before
+// it; vector-memory traffic (the LDS DMA) is waited for separately with wait_vmcnt.
+__device__ __forceinline__ void barrier_lds() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+}
+
+// Enqueue the B x D bf16 tile at `src` (row-major) into LDS at byte address `lds_addr` by
+// LDS DMA (global_load_lds_dwordx4: each lane's 16 bytes land at M0 + 16*lane).  Wave w
+// writes chunks [w*TI*64, (w+1)*TI*64) of the tile, i.e. 64/KCH whole rows per instruction,
+// fetching for each LDS chunk the global chunk the swizzle maps there.  Rows past N of the
+// last block are read too (they lie inside the Npad-row tensor; the caller masks them).
+// Issued as inline assembly so that the compiler does not serialise every later LDS read
+// behind it; completion is awaited explicitly with wait_vmcnt (vector-memory operations
+// retire in order).
+template <int D, int B, bool IS_V>
+__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint32_t lds_addr,
+                                         int wv, int lane) {
     using Tl = Tile<D, B>;
-    constexpr int KP = D + 8, VP = B + 8;
-    constexpr int PAIRS = Tl::LOADS / 2;   // key pairs per thread
-    const int t = threadIdx.x;
-    const int64_t row0 = (int64_t)blk * B;
-    const uint4* kg = (const uint4*)(a.k + (bh * a.Npad + row0) * D);
-    const uint4* vg = (const uint4*)(a.v + (bh * a.Npad + row0) * D);
-    const int64_t nreal = a.N - row0;
+    constexpr int RPI = 64 / Tl::KCH;                        // rows per instruction
+    const uint64_t sp = (uint64_t)(size_t)src;               // wave-uniform: SGPR pair
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)sp);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(sp >> 32));
+    const uint16_t* sbase = (const uint16_t*)(size_t)(((uint64_t)hi << 32) | lo);
+    const int lr = lane / Tl::KCH;                           // row inside the instruction
+    const int pc = lane % Tl::KCH;                           // LDS chunk inside the row
 #pragma unroll
-    for (int u = 0; u < PAIRS; ++u) {
-        const int c = t + Tl::NT * u;            // pair-chunk index
-        const int key = 2 * (c / Tl::KCH);       // even key of the pair
-        const int ch = c % Tl::KCH;
-        const bool ok0 = key < nreal, ok1 = key + 1 < nreal;
-        const uint4 k0 = ok0 ? kg[key * Tl::KCH + ch] : make_uint4(0, 0, 0, 0);
-        const uint4 k1 = ok1 ? kg[(key + 1) * Tl::KCH + ch] : make_uint4(0, 0, 0, 0);
-        const uint4 v0 = ok0 ? vg[key * Tl::KCH + ch] : make_uint4(0, 0, 0, 0);
-        const uint4 v1 = ok1 ? vg[(key + 1) * Tl::KCH + ch] : make_uint4(0, 0, 0, 0);
-        *(uint4*)(Ks + key * KP + ch * 8) = k0;
-        *(uint4*)(Ks + (key + 1) * KP + ch * 8) = k1;
-        uint32_t* vt = (uint32_t*)(Vt + (ch * 8) * VP + vslot(key));
-        const uint32_t a0[4] = {v0.x, v0.y, v0.z, v0.w};
-        const uint32_t a1[4] = {v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            // d = 8 ch + 2e: low halves; d + 1: high halves
-            vt[(2 * e) * (VP / 2)] = __builtin_amdgcn_perm(a1[e], a0[e], 0x05040100u);
-            vt[(2 * e + 1) * (VP / 2)] = __builtin_amdgcn_perm(a1[e], a0[e], 0x07060302u);
-        }
+    for (int u = 0; u < Tl::TI; ++u) {
+        const int r0 = (wv * Tl::TI + u) * RPI;              // first row (uniform)
+        const int r = r0 + lr;
+        const int lc = pc ^ (IS_V ? swz_v<Tl::KCH>(r) : swz_k<Tl::KCH>(r));
+        const uint32_t voff = (uint32_t)((lr * D + lc * 8) * 2);
+        const uint16_t* rowbase = sbase + r0 * D;
+        const uint32_t m0 = lds_addr + (uint32_t)((wv * Tl::TI + u) * 64 * 16);
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :
+                     : "s"(m0), "v"(voff), "s"(rowbase)
+                     : "memory", "m0");
     }
 }
 
 // Merge the unnormalised partials (O_s, m_s, l_s) of a split row in chunk order:
 // O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
 template <int D, int B>
-__device__ __noinline__ void combine_split(const AttnArgs& a, int64_t bh, int32_t iblk,
+__device__ __noinline__ void combine_split(const float* __restrict__ part_o,
+                                           const float* __restrict__ part_ml,
+                                           uint16_t* __restrict__ out, float* __restrict__ lse,
+                                           int64_t N, int64_t Npad, int64_t bh, int32_t iblk,
                                            int32_t slot0, int32_t nchunk) {
     constexpr int NT = Tile<D, B>::NT;
     for (int idx = threadIdx.x; idx < B * D; idx += NT) {
@@ -317,18 +343,18 @@ __device__ __noinline__ void combine_split(const AttnArgs& a, int64_t bh, int32_
         const int64_t qp = (int64_t)iblk * B + qq;
         float M = -INFINITY;
         for (int c = 0; c < nchunk; ++c)
-            M = fmaxf(M, a.part_ml[((int64_t)(slot0 + c) * B + qq) * 2]);
+            M = fmaxf(M, part_ml[((int64_t)(slot0 + c) * B + qq) * 2]);
         float num = 0.f, den = 0.f;
         for (int c = 0; c < nchunk; ++c) {
             const int64_t sl = slot0 + c;
-            const float w = __builtin_amdgcn_exp2f(a.part_ml[(sl * B + qq) * 2] - M);
-            num = fmaf(w, a.part_o[(sl * B + qq) * D + d], num);
-            den = fmaf(w, a.part_ml[(sl * B + qq) * 2 + 1], den);
+            const float w = __builtin_amdgcn_exp2f(part_ml[(sl * B + qq) * 2] - M);
+            num = fmaf(w, part_o[(sl * B + qq) * D + d], num);
+            den = fmaf(w, part_ml[(sl * B + qq) * 2 + 1], den);
         }
-        const bool real = qp < a.N;
-        a.out[(bh * a.Npad + qp) * D + d] = (real && den > 0.f) ? f2bf(num / den) : (uint16_t)0;
-        if (d == 0 && a.lse)
-            a.lse[bh * a.Npad + qp] =
+        const bool real = qp < N;
+        out[(bh * Npad + qp) * D + d] = (real && den > 0.f) ? f2bf(num / den) : (uint16_t)0;
+        if (d == 0 && lse)
+            lse[bh * Npad + qp] =
                 (real && den > 0.f) ? (M + __log2f(den)) * 0.69314718055994531f : 0.f;
     }
 }
@@ -336,33 +362,54 @@ __device__ __noinline__ void combine_split(const AttnArgs& a, int64_t bh, int32_
 template <int D, int B>
 __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
     using Tl = Tile<D, B>;
-    __shared__ __align__(16) uint16_t Ks[B * (D + 8)];
-    __shared__ __align__(16) uint16_t Vt[D * (B + 8)];
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    __shared__ __align__(1024) uint16_t Ks[B * D];
+    __shared__ __align__(1024) uint16_t Vs[B * D];
     __shared__ int s_pop;
 
     const int t = threadIdx.x;
     const int lane = t & 63;
-    const int wv = t >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform, kept in an SGPR
     const int half = lane >> 5;      // 0 / 1
     const int l32 = lane & 31;
     const int q0 = xcc_id() % kNQ;
-    const int32_t Kc = a.hdr[kHdrKc];
+    const int32_t Kc = ld_const(a.hdr, kHdrKc);
+
+    // per-lane LDS byte offsets of the MFMA operand reads (constant over the whole kernel)
+    //  K (A of S^T): row 32 tt + l32, logical chunk 2 kk + half
+    //  V (A of O^T, transposed read): 16-lane group g = lane / 16 reads rows
+    //    32 t + 16 m + 8 s + 4 half + j / 4 (j = lane % 16) at columns 32 dt + 16 (g % 2) + 4 (j % 4)
+    const int j16 = lane & 15;
+    const int g16 = lane >> 4;
+    const int vrow0 = 4 * half + (j16 >> 2);               // row inside a 16-row step, s = 0
+    const int vsw = swz_v<Tl::KCH>(vrow0);                 // same for every step (2r mod KCH)
+    typedef __attribute__((address_space(3))) char lds_char;
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    lds_char* const vs_lds = (lds_char*)Vs;
+    const uint32_t ks_addr = (uint32_t)(size_t)(lds_char*)Ks;
+    const uint32_t vs_addr = (uint32_t)(size_t)vs_lds;
 
     for (int qo = 0; qo < kNQ; ++qo) {
         const int qi = (q0 + qo) % kNQ;
-        const int32_t qlen = a.hdr[kHdrQLen + qi];
-        const int32_t qstart = a.hdr[kHdrQStart + qi];
+        const int32_t qlen = ld_const(a.hdr, kHdrQLen + qi);
+        const int32_t qstart = ld_const(a.hdr, kHdrQStart + qi);
         while (true) {
             if (t == 0) s_pop = atomicAdd(&a.ctr[32 * qi], 1);
             __syncthreads();
-            const int32_t pop = s_pop;
+            const int32_t pop = __builtin_amdgcn_readfirstlane(s_pop);
             __syncthreads();
             if (pop >= qlen) break;
-            const int4 it = a.items[qstart + pop];
+            int4 it = ld_const4(a.items, qstart + pop);
+            it.x = __builtin_amdgcn_readfirstlane(it.x);        // the item is workgroup-uniform
+            it.y = __builtin_amdgcn_readfirstlane(it.y);
+            it.z = __builtin_amdgcn_readfirstlane(it.z);
+            it.w = __builtin_amdgcn_readfirstlane(it.w);
             const int64_t row = it.x;
             const int64_t bh = row / a.n_blk;
             const int32_t iblk = (int32_t)(row - bh * a.n_blk);
             const int64_t qrow0 = (int64_t)iblk * B + wv * 32;   // first query row of wave
+            const uint16_t* kbase = a.k + bh * a.Npad * D;
+            const uint16_t* vbase = a.v + bh * a.Npad * D;
 
             // Q^T operand: lane holds query l32, d = 16 kk + 8 half .. +8
             bf16x8 qf[Tl::NKK];
@@ -375,6 +422,16 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
                     qf[kk] = __builtin_bit_cast(bf16x8, raw);
                 }
             }
+            // Q is in registers before the first LDS DMA of the item is issued, so the only
+            // vector-memory operations in flight inside the block loop are the DMA tiles
+            wait_vmcnt(0);
+            // first key block of the item into LDS
+            {
+                const int32_t blk = ld_const(a.col_idx, it.y);
+                dma_tile<D, B, false>(kbase + (int64_t)blk * B * D, ks_addr, wv, lane);
+                dma_tile<D, B, true>(vbase + (int64_t)blk * B * D, vs_addr, wv, lane);
+            }
+
             f32x16 o[Tl::NDT];
 #pragma unroll
             for (int dt = 0; dt < Tl::NDT; ++dt)
@@ -383,24 +440,31 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
             float m = -INFINITY, l = 0.f;
 
             for (int32_t e = it.y; e < it.z; ++e) {
-                const int32_t blk = a.col_idx[e];
-                __syncthreads();                       // previous tile fully consumed
-                load_kv<D, B>(a, bh, blk, Ks, Vt);
-                __syncthreads();
+                const int32_t blk = ld_const(a.col_idx, e);
+                const bool more = e + 1 < it.z;
+                const int32_t nblk = more ? ld_const(a.col_idx, e + 1) : blk;
+                // K_e is in LDS once this wave's DMA older than V_e has landed
+                wait_vmcnt(Tl::TI);
+                barrier_lds();
                 // S^T = K Q^T
                 f32x16 s[Tl::NKT];
 #pragma unroll
-                for (int tt = 0; tt < Tl::NKT; ++tt) {
+                for (int tt = 0; tt < Tl::NKT; ++tt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) s[tt][r] = 0.f;
-                    const int key = 32 * tt + l32;
 #pragma unroll
-                    for (int kk = 0; kk < Tl::NKK; ++kk) {
-                        const bf16x8 kf =
-                            *(const bf16x8*)(Ks + key * (D + 8) + (2 * kk + half) * 8);
+                for (int kk = 0; kk < Tl::NKK; ++kk) {
+                    const int pch = (2 * kk + half) ^ swz_k<Tl::KCH>(l32);
+#pragma unroll
+                    for (int tt = 0; tt < Tl::NKT; ++tt) {
+                        const bf16x8 kf = *(const bf16x8*)(Ks + (32 * tt + l32) * D + pch * 8);
                         s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[tt], 0, 0, 0);
                     }
                 }
+                barrier_lds();                           // every wave is done with K_e
+                // K_{e+1} (the last block re-fetches K_e, which keeps the DMA count per
+                // iteration constant so the wait below needs no branch)
+                dma_tile<D, B, false>(kbase + (int64_t)nblk * B * D, ks_addr, wv, lane);
                 // pad keys of a short last block
                 if (a.N - (int64_t)blk * B < B) {
                     const int lim = (int)(a.N - (int64_t)blk * B) - 4 * half;
@@ -440,17 +504,28 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
                             l += p;
                             pf[2 * tt + hh][e8] = (__bf16)p;
                         }
-                // O^T += V^T P^T
+                // V_e landed (the K tile issued after it may still be in flight)
+                wait_vmcnt(Tl::TI);
+                barrier_lds();
+                // O^T += V^T P^T; V^T operand by transposed LDS reads of row-major V
 #pragma unroll
                 for (int dt = 0; dt < Tl::NDT; ++dt) {
-                    const int d = 32 * dt + l32;
+                    const int lc = 4 * dt + 2 * (g16 & 1) + ((j16 & 3) >> 1);
+                    const uint32_t col_off = (uint32_t)(((lc ^ vsw) * 16) + (j16 & 1) * 8);
 #pragma unroll
                     for (int ks = 0; ks < Tl::NPK; ++ks) {
-                        const bf16x8 vf =
-                            *(const bf16x8*)(Vt + d * (B + 8) + (2 * ks + half) * 8);
+                        const int r0 = 16 * ks + vrow0;          // row for s = 0; s = 1 adds 8
+                        lds_char* p0 = vs_lds + r0 * D * 2 + col_off;
+                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+                        const s16x4 hi =
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * D * 2));
+                        const bf16x8 vf = __builtin_bit_cast(
+                            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[dt], 0, 0, 0);
                     }
                 }
+                barrier_lds();                           // every wave is done with V_e
+                if (more) dma_tile<D, B, true>(vbase + (int64_t)nblk * B * D, vs_addr, wv, lane);
             }
 
             const float lt = l + __shfl_xor(l, 32, 64);
@@ -504,7 +579,8 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
                 if (prev == nchunk - 1) {
                     // last chunk to finish: merge all partials in chunk order
                     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                    combine_split<D, B>(a, bh, iblk, it.w, nchunk);
+                    combine_split<D, B>(a.part_o, a.part_ml, a.out, a.lse, a.N, a.Npad, bh, iblk,
+                                        it.w, nchunk);
                 }
             }
         }
