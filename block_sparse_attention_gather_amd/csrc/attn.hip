@@ -274,18 +274,25 @@ struct Tile {
 // 16-byte-chunk swizzles of the row-major K and V tiles in LDS (row r, logical chunk c is
 // stored at chunk c ^ swz(r) of row r):
 //  K: the 32 lanes of a half-wave read rows r..r+31 at one chunk (ds_read_b128), so
-//     swz(r) = r mod chunks puts any 8 consecutive rows on 8 distinct bank groups;
-//  V: a 16-lane group of ds_read_b64_tr_b16 reads 4 consecutive rows x 2 adjacent chunks,
-//     so swz(r) = 2r mod chunks keeps those 8 chunks on 8 distinct bank groups.
+//     swz(r) = r mod chunks puts any 16 consecutive rows on 16 distinct bank groups;
+//  V: ds_read_b64_tr_b16 is served 32 lanes at a time from 64 banks; one half-wave reads 4
+//     consecutive rows x 4 adjacent chunks, and swz(r) = 4r mod chunks places those 16
+//     chunks on 16 distinct bank groups (measured: no bank-conflict cycles on gfx950).
 template <int KCH> __device__ __forceinline__ int swz_k(int r) { return r & (KCH - 1); }
-template <int KCH> __device__ __forceinline__ int swz_v(int r) { return (2 * r) & (KCH - 1); }
+template <int KCH> __device__ __forceinline__ int swz_v(int r) { return (4 * r) & (KCH - 1); }
 
+// s_waitcnt vmcnt(N) with expcnt / lgkmcnt left unconstrained (gfx9 encoding: vmcnt bits
+// [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
 __device__ __forceinline__ void wait_vmcnt(int n) {
-    // s_waitcnt vmcnt(n) with expcnt / lgkmcnt left unconstrained (gfx9 encoding)
-    if (n == 0) __builtin_amdgcn_s_waitcnt(0x0f70);
-    else if (n == 4) __builtin_amdgcn_s_waitcnt(0x0f74);
-    else if (n == 8) __builtin_amdgcn_s_waitcnt(0x0f78);
-    else __builtin_amdgcn_s_waitcnt(0x0f70);
+    if (n == 0) wait_vm<0>();
+    else if (n == 4) wait_vm<4>();
+    else if (n == 8) wait_vm<8>();
+    else wait_vm<0>();
 }
 
 // Workgroup barrier that also orders this wave's LDS reads (ds_read results consumed) before
@@ -461,6 +468,7 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
                         s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[tt], 0, 0, 0);
                     }
                 }
+                wait_vmcnt(0);                           // V_e landed too
                 barrier_lds();                           // every wave is done with K_e
                 // K_{e+1} (the last block re-fetches K_e, which keeps the DMA count per
                 // iteration constant so the wait below needs no branch)
@@ -492,9 +500,11 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
                         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
                     m = mn;
                 }
+                // softmax of key tile tt (VALU) and O^T += V^T P^T for key tile tt - 1 (MFMA)
+                // are independent, so the two streams interleave; the V^T operand comes from
+                // transposed LDS reads of row-major V
                 bf16x8 pf[Tl::NPK];
-#pragma unroll
-                for (int tt = 0; tt < Tl::NKT; ++tt)
+                auto softmax_tile = [&](int tt) {
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -504,26 +514,33 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
                             l += p;
                             pf[2 * tt + hh][e8] = (__bf16)p;
                         }
-                // V_e landed (the K tile issued after it may still be in flight)
-                wait_vmcnt(Tl::TI);
-                barrier_lds();
-                // O^T += V^T P^T; V^T operand by transposed LDS reads of row-major V
+                };
+                auto pv_tile = [&](int tt) {
 #pragma unroll
-                for (int dt = 0; dt < Tl::NDT; ++dt) {
-                    const int lc = 4 * dt + 2 * (g16 & 1) + ((j16 & 3) >> 1);
-                    const uint32_t col_off = (uint32_t)(((lc ^ vsw) * 16) + (j16 & 1) * 8);
+                    for (int ks = 2 * tt; ks < 2 * tt + 2; ++ks)
 #pragma unroll
-                    for (int ks = 0; ks < Tl::NPK; ++ks) {
-                        const int r0 = 16 * ks + vrow0;          // row for s = 0; s = 1 adds 8
-                        lds_char* p0 = vs_lds + r0 * D * 2 + col_off;
-                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-                        const s16x4 hi =
-                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * D * 2));
-                        const bf16x8 vf = __builtin_bit_cast(
-                            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[dt], 0, 0, 0);
-                    }
+                        for (int dt = 0; dt < Tl::NDT; ++dt) {
+                            const int lc = 4 * dt + 2 * (g16 & 1) + ((j16 & 3) >> 1);
+                            const uint32_t col_off =
+                                (uint32_t)(((lc ^ vsw) * 16) + (j16 & 1) * 8);
+                            lds_char* p0 = vs_lds + (16 * ks + vrow0) * D * 2 + col_off;
+                            const s16x4 lo =
+                                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+                            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (lds_s16x4*)(p0 + 8 * D * 2));
+                            const bf16x8 vf = __builtin_bit_cast(
+                                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[dt], 0,
+                                                                            0, 0);
+                        }
+                };
+                softmax_tile(0);
+#pragma unroll
+                for (int tt = 1; tt < Tl::NKT; ++tt) {
+                    softmax_tile(tt);
+                    pv_tile(tt - 1);
                 }
+                pv_tile(Tl::NKT - 1);
                 barrier_lds();                           // every wave is done with V_e
                 if (more) dma_tile<D, B, true>(vbase + (int64_t)nblk * B * D, vs_addr, wv, lane);
             }

@@ -5,7 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/bsa.h"
+#include "bsa.h"
 
 namespace bsa {
 
