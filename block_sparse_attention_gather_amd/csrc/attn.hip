@@ -336,6 +336,43 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint3
     }
 }
 
+// One instruction (u) of dma_tile, for spreading a tile's DMA between compute instructions.
+// No memory clobber: LDS reads of the other buffer may be scheduled across it, while the
+// volatile statement keeps its place relative to barriers and waits.
+template <int D, int B, bool IS_V>
+__device__ __forceinline__ void dma_part(const uint16_t* sbase, uint32_t lds_addr, int wv,
+                                         int lane, int u) {
+    using Tl = Tile<D, B>;
+    constexpr int RPI = 64 / Tl::KCH;
+    const int lr = lane / Tl::KCH;
+    const int pc = lane % Tl::KCH;
+    const int r0 = (wv * Tl::TI + u) * RPI;
+    const int r = r0 + lr;
+    const int lc = pc ^ (IS_V ? swz_v<Tl::KCH>(r) : swz_k<Tl::KCH>(r));
+    const uint32_t voff = (uint32_t)((lr * D + lc * 8) * 2);
+    const uint16_t* rowbase = sbase + r0 * D;
+    const uint32_t m0 = lds_addr + (uint32_t)((wv * Tl::TI + u) * 64 * 16);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(m0), "v"(voff), "s"(rowbase)
+                 : "m0");
+}
+
+// Value held by lane l ^ 32 (the other half of the wavefront), via v_permlane32_swap.
+__device__ __forceinline__ float other_half(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// A wave-uniform pointer kept in an SGPR pair (the saddr operand of the DMA).
+__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
+    const uint64_t sp = (uint64_t)(size_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)sp);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(sp >> 32));
+    return (const uint16_t*)(size_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Merge the unnormalised partials (O_s, m_s, l_s) of a split row in chunk order:
 // O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
 template <int D, int B>
@@ -433,11 +470,8 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
             // vector-memory operations in flight inside the block loop are the DMA tiles
             wait_vmcnt(0);
             // first key block of the item into LDS
-            {
-                const int32_t blk = ld_const(a.col_idx, it.y);
-                dma_tile<D, B, false>(kbase + (int64_t)blk * B * D, ks_addr, wv, lane);
-                dma_tile<D, B, true>(vbase + (int64_t)blk * B * D, vs_addr, wv, lane);
-            }
+            dma_tile<D, B, false>(kbase + (int64_t)ld_const(a.col_idx, it.y) * B * D, ks_addr, wv,
+                                  lane);
 
             f32x16 o[Tl::NDT];
 #pragma unroll
@@ -449,9 +483,12 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
             for (int32_t e = it.y; e < it.z; ++e) {
                 const int32_t blk = ld_const(a.col_idx, e);
                 const bool more = e + 1 < it.z;
-                const int32_t nblk = more ? ld_const(a.col_idx, e + 1) : blk;
-                // K_e is in LDS once this wave's DMA older than V_e has landed
-                wait_vmcnt(Tl::TI);
+                const uint16_t* vsrc = uniform_ptr(vbase + (int64_t)blk * B * D);
+                const uint16_t* ksrc =
+                    uniform_ptr(kbase + (int64_t)(more ? ld_const(a.col_idx, e + 1) : blk) * B * D);
+                // K_e landed (the only DMA in flight); after the barrier every wave is done
+                // with V_{e-1}, so V_e streams into the V buffer during the first half of S_e
+                wait_vm<0>();
                 barrier_lds();
                 // S^T = K Q^T
                 f32x16 s[Tl::NKT];
@@ -467,12 +504,12 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
                         const bf16x8 kf = *(const bf16x8*)(Ks + (32 * tt + l32) * D + pch * 8);
                         s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[tt], 0, 0, 0);
                     }
+#pragma unroll
+                    for (int u = kk * 2 * Tl::TI / Tl::NKK; u < (kk + 1) * 2 * Tl::TI / Tl::NKK; ++u)
+                        if (u < Tl::TI) dma_part<D, B, true>(vsrc, vs_addr, wv, lane, u);
                 }
-                wait_vmcnt(0);                           // V_e landed too
-                barrier_lds();                           // every wave is done with K_e
-                // K_{e+1} (the last block re-fetches K_e, which keeps the DMA count per
-                // iteration constant so the wait below needs no branch)
-                dma_tile<D, B, false>(kbase + (int64_t)nblk * B * D, ks_addr, wv, lane);
+                wait_vm<0>();                            // V_e landed
+                barrier_lds();                           // V_e visible; every wave done with K_e
                 // pad keys of a short last block
                 if (a.N - (int64_t)blk * B < B) {
                     const int lim = (int)(a.N - (int64_t)blk * B) - 4 * half;
@@ -488,7 +525,7 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
                 for (int tt = 0; tt < Tl::NKT; ++tt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tt][r]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                mx = fmaxf(mx, other_half(mx));
                 const float mnew = mx * a.scale_log2;
                 if (__any(mnew > m + kRescaleThresh)) {
                     const float mn = fmaxf(m, mnew);
@@ -534,18 +571,25 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
                                                                             0, 0);
                         }
                 };
+                // K_{e+1} streams into the K buffer while the softmax and PV run
+                constexpr int KPT = Tl::TI / Tl::NKT;    // K DMA instructions per key tile
                 softmax_tile(0);
+                if (more)
+#pragma unroll
+                    for (int u = 0; u < KPT; ++u) dma_part<D, B, false>(ksrc, ks_addr, wv, lane, u);
 #pragma unroll
                 for (int tt = 1; tt < Tl::NKT; ++tt) {
                     softmax_tile(tt);
                     pv_tile(tt - 1);
+                    if (more)
+#pragma unroll
+                        for (int u = tt * KPT; u < (tt + 1) * KPT; ++u)
+                            dma_part<D, B, false>(ksrc, ks_addr, wv, lane, u);
                 }
                 pv_tile(Tl::NKT - 1);
-                barrier_lds();                           // every wave is done with V_e
-                if (more) dma_tile<D, B, true>(vbase + (int64_t)nblk * B * D, vs_addr, wv, lane);
             }
 
-            const float lt = l + __shfl_xor(l, 32, 64);
+            const float lt = l + other_half(l);
             const int64_t qpos = qrow0 + l32;
             if (it.w < 0) {
                 // whole row in this item: normalise and store
