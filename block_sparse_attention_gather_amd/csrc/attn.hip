@@ -403,6 +403,23 @@ __device__ __noinline__ void combine_split(const float* __restrict__ part_o,
     }
 }
 
+// Scheduling pin for an operand pipeline of NM MFMAs that each consume R LDS reads: the reads
+// of the first kPrefetch MFMAs go first, then every MFMA is followed by the reads of the MFMA
+// kPrefetch places later, so each MFMA's operands were requested about kPrefetch MFMAs (~130
+// cycles of matrix-core work) before it issues instead of immediately before it.
+constexpr int kPrefetch = 4;
+template <int NM, int R>
+__device__ __forceinline__ void pin_pipeline() {
+    __builtin_amdgcn_sched_group_barrier(0x100, R * kPrefetch, 0);     // DS reads
+#pragma unroll
+    for (int i = 0; i < NM - kPrefetch; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kPrefetch; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+}
+
 template <int D, int B>
 __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
     using Tl = Tile<D, B>;
@@ -496,17 +513,29 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
                 for (int tt = 0; tt < Tl::NKT; ++tt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) s[tt][r] = 0.f;
+                {
+                    // K operands are read kPrefetch MFMAs ahead of their use (order pinned
+                    // below); the V DMA parts go out during the first half of the reads
+                    constexpr int NM = Tl::NKK * Tl::NKT;
+                    bf16x8 kf[NM];
 #pragma unroll
-                for (int kk = 0; kk < Tl::NKK; ++kk) {
-                    const int pch = (2 * kk + half) ^ swz_k<Tl::KCH>(l32);
+                    for (int i = 0; i < NM; ++i) {
+                        const int kk = i / Tl::NKT, tt = i % Tl::NKT;
+                        const int pch = (2 * kk + half) ^ swz_k<Tl::KCH>(l32);
+                        kf[i] = *(const bf16x8*)(Ks + (32 * tt + l32) * D + pch * 8);
+                        if (tt == Tl::NKT - 1) {
 #pragma unroll
-                    for (int tt = 0; tt < Tl::NKT; ++tt) {
-                        const bf16x8 kf = *(const bf16x8*)(Ks + (32 * tt + l32) * D + pch * 8);
-                        s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[tt], 0, 0, 0);
+                            for (int u = kk * 2 * Tl::TI / Tl::NKK;
+                                 u < (kk + 1) * 2 * Tl::TI / Tl::NKK; ++u)
+                                if (u < Tl::TI) dma_part<D, B, true>(vsrc, vs_addr, wv, lane, u);
+                        }
                     }
 #pragma unroll
-                    for (int u = kk * 2 * Tl::TI / Tl::NKK; u < (kk + 1) * 2 * Tl::TI / Tl::NKK; ++u)
-                        if (u < Tl::TI) dma_part<D, B, true>(vsrc, vs_addr, wv, lane, u);
+                    for (int i = 0; i < NM; ++i) {
+                        const int kk = i / Tl::NKT, tt = i % Tl::NKT;
+                        s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[kk], s[tt], 0, 0, 0);
+                    }
+                    pin_pipeline<NM, 1>();
                 }
                 wait_vm<0>();                            // V_e landed
                 barrier_lds();                           // V_e visible; every wave done with K_e
@@ -537,9 +566,8 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
                         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
                     m = mn;
                 }
-                // softmax of key tile tt (VALU) and O^T += V^T P^T for key tile tt - 1 (MFMA)
-                // are independent, so the two streams interleave; the V^T operand comes from
-                // transposed LDS reads of row-major V
+                // softmax of the block (VALU), then O^T += V^T P^T (MFMA) with the V^T operands
+                // read from row-major V by transposed LDS reads, kPrefetch MFMAs ahead
                 bf16x8 pf[Tl::NPK];
                 auto softmax_tile = [&](int tt) {
 #pragma unroll
@@ -552,41 +580,40 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
                             pf[2 * tt + hh][e8] = (__bf16)p;
                         }
                 };
-                auto pv_tile = [&](int tt) {
-#pragma unroll
-                    for (int ks = 2 * tt; ks < 2 * tt + 2; ++ks)
-#pragma unroll
-                        for (int dt = 0; dt < Tl::NDT; ++dt) {
-                            const int lc = 4 * dt + 2 * (g16 & 1) + ((j16 & 3) >> 1);
-                            const uint32_t col_off =
-                                (uint32_t)(((lc ^ vsw) * 16) + (j16 & 1) * 8);
-                            lds_char* p0 = vs_lds + (16 * ks + vrow0) * D * 2 + col_off;
-                            const s16x4 lo =
-                                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-                            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (lds_s16x4*)(p0 + 8 * D * 2));
-                            const bf16x8 vf = __builtin_bit_cast(
-                                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[dt], 0,
-                                                                            0, 0);
-                        }
-                };
-                // K_{e+1} streams into the K buffer while the softmax and PV run
+                // K_{e+1} streams into the K buffer (every wave finished S_e before the last
+                // barrier) while the softmax and PV run
                 constexpr int KPT = Tl::TI / Tl::NKT;    // K DMA instructions per key tile
-                softmax_tile(0);
-                if (more)
 #pragma unroll
-                    for (int u = 0; u < KPT; ++u) dma_part<D, B, false>(ksrc, ks_addr, wv, lane, u);
-#pragma unroll
-                for (int tt = 1; tt < Tl::NKT; ++tt) {
+                for (int tt = 0; tt < Tl::NKT; ++tt) {
                     softmax_tile(tt);
-                    pv_tile(tt - 1);
                     if (more)
 #pragma unroll
                         for (int u = tt * KPT; u < (tt + 1) * KPT; ++u)
                             dma_part<D, B, false>(ksrc, ks_addr, wv, lane, u);
                 }
-                pv_tile(Tl::NKT - 1);
+                {
+                    constexpr int NM = Tl::NPK * Tl::NDT;
+                    bf16x8 vfr[NM];
+#pragma unroll
+                    for (int i = 0; i < NM; ++i) {
+                        const int ks = i / Tl::NDT, dt = i % Tl::NDT;
+                        const int lc = 4 * dt + 2 * (g16 & 1) + ((j16 & 3) >> 1);
+                        const uint32_t col_off = (uint32_t)(((lc ^ vsw) * 16) + (j16 & 1) * 8);
+                        lds_char* p0 = vs_lds + (16 * ks + vrow0) * D * 2 + col_off;
+                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+                        const s16x4 hi =
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * D * 2));
+                        vfr[i] = __builtin_bit_cast(
+                            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    }
+#pragma unroll
+                    for (int i = 0; i < NM; ++i) {
+                        const int ks = i / Tl::NDT, dt = i % Tl::NDT;
+                        o[dt] =
+                            __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[i], pf[ks], o[dt], 0, 0, 0);
+                    }
+                    pin_pipeline<NM, 2>();
+                }
             }
 
             const float lt = l + other_half(l);
