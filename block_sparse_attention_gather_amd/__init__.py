@@ -20,6 +20,7 @@ from typing import Optional, Tuple
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libbsa.so")
+TRACE_LIB_PATH = os.path.join(_PKG, "libbsa_trace.so")   # debug build with bsa_trace_read
 
 BSA_OK = 0
 _STATUS = {-1: "BSA_ERR_INVALID_ARG", -2: "BSA_ERR_UNSUPPORTED", -3: "BSA_ERR_WORKSPACE",
@@ -105,6 +106,40 @@ def _load():
 def lib():
     """The loaded ctypes library (raises if it is not built)."""
     return _load()
+
+
+def load_library(path: str):
+    """Route every later call through another build of libbsa (e.g. TRACE_LIB_PATH)."""
+    global _lib, LIB_PATH
+    LIB_PATH = path
+    _lib = None
+    return _load()
+
+
+# one record per attention workgroup (debug build): s_memrealtime ticks (100 MHz) at entry,
+# after the last work item and at exit; s_memtime (shader clock) ticks at entry and exit;
+# HW_REG_HW_ID and XCC id; items and key blocks done
+TRACE_DTYPE = [("t0", "<u8"), ("t_last", "<u8"), ("t_end", "<u8"), ("c0", "<u8"),
+               ("c_end", "<u8"), ("hw_id", "<u4"), ("xcc", "<u4"), ("items", "<i4"),
+               ("blocks", "<i4")]
+TRACE_MAX = 8192
+
+
+def trace_read(count: int = TRACE_MAX):
+    """Workgroup records of the latest attention launch (needs libbsa_trace.so loaded).
+    Synchronous.  Returns a NumPy structured array with the records that were written."""
+    import numpy as np
+    lib = _load()
+    if not hasattr(lib, "bsa_trace_read"):
+        raise BsaError(-1, f"{LIB_PATH} is not a trace build")
+    fn = lib.bsa_trace_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+    buf = np.zeros(count, dtype=TRACE_DTYPE)
+    rc = fn(buf.ctypes.data, count)
+    if rc != 0:
+        raise BsaError(-4, f"bsa_trace_read failed ({rc})")
+    return buf[buf["t_end"] != 0]
 
 
 def version() -> str:

@@ -1,9 +1,12 @@
 """Build libbsa.so (HIP for gfx950) in-tree.
 
-    python -m block_sparse_attention_gather_amd.build [--jobs N] [--verbose]
+    python -m block_sparse_attention_gather_amd.build [--jobs N] [--verbose] [--no-trace]
 
 Each .hip translation unit is compiled to an object in parallel, then linked into
-block_sparse_attention_gather_amd/libbsa.so.  Always recompiles (a build check must compile).
+block_sparse_attention_gather_amd/libbsa.so.  The same sources with -DBSA_TRACE (per-workgroup
+timestamps of the attention launch, read back with bsa_trace_read) are linked into
+libbsa_trace.so, a debug library for load-balance measurements.  Always recompiles (a build
+check must compile).
 """
 from __future__ import annotations
 
@@ -19,11 +22,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbsa.so")
+TRACE_LIB = os.path.join(PKG, "libbsa_trace.so")
 SOURCES = ["api.hip", "reorder.hip", "route.hip", "attn.hip"]
 ARCH = os.environ.get("BSA_OFFLOAD_ARCH", "gfx950")
 
 CFLAGS = [
-    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=hidden",
     "-I", os.path.join(ROOT, "include"),
     # packed fp32 ops (v_pk_*_f32) are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -50,7 +54,13 @@ def _run(cmd, verbose):
         print(out)
 
 
-def build(jobs: int = 0, verbose: bool = False) -> str:
+def _link(cc, objs, lib, verbose):
+    tmp = lib + ".tmp"
+    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int = 0, verbose: bool = False, trace: bool = True) -> str:
     cc = hipcc()
     os.makedirs(BUILD, exist_ok=True)
     objs = []
@@ -59,11 +69,16 @@ def build(jobs: int = 0, verbose: bool = False) -> str:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
         cmds.append([cc, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    trace_obj = os.path.join(BUILD, "attn_trace.o")
+    if trace:
+        cmds.append([cc, *CFLAGS, "-DBSA_TRACE", "-c", os.path.join(CSRC, "attn.hip"), "-o",
+                     trace_obj])
     with ThreadPoolExecutor(jobs or min(len(cmds), os.cpu_count() or 1)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB + ".tmp"
-    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
+    _link(cc, objs, LIB, verbose)
+    if trace:
+        _link(cc, [o for o in objs if not o.endswith("attn.o")] + [trace_obj], TRACE_LIB,
+              verbose)
     return LIB
 
 
@@ -71,8 +86,9 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=0)
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--no-trace", action="store_true", help="skip libbsa_trace.so")
     a = ap.parse_args(argv)
-    print(build(a.jobs, a.verbose))
+    print(build(a.jobs, a.verbose, trace=not a.no_trace))
 
 
 if __name__ == "__main__":

@@ -218,6 +218,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_rows_kernel(
 // ---------------------------------------------------------------------------------------
 // attention
 // ---------------------------------------------------------------------------------------
+#ifdef BSA_TRACE
+// Debug build only (libbsa_trace.so): one record per workgroup of the latest attention launch,
+// s_memrealtime (100 MHz) stamps at kernel entry, after the workgroup's last work item and at
+// exit, s_memtime (shader clock) stamps at entry and exit, the hardware placement and the work
+// done.  Read with bsa_trace_read().
+constexpr int kTraceMax = 8192;
+struct TraceRec {
+    unsigned long long t0, t_last, t_end, c0, c_end;
+    uint32_t hw_id, xcc;
+    int32_t items, blocks;
+};
+__device__ TraceRec g_trace_rec[kTraceMax];
+#endif
+
 struct AttnArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -435,6 +449,12 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
     const int l32 = lane & 31;
     const int q0 = xcc_id() % kNQ;
     const int32_t Kc = ld_const(a.hdr, kHdrKc);
+#ifdef BSA_TRACE
+    const unsigned long long tr_t0 = __builtin_amdgcn_s_memrealtime();
+    const unsigned long long tr_c0 = __builtin_amdgcn_s_memtime();
+    unsigned long long tr_last = tr_t0;
+    int32_t tr_items = 0, tr_blocks = 0;
+#endif
 
     // per-lane LDS byte offsets of the MFMA operand reads (constant over the whole kernel)
     //  K (A of S^T): row 32 tt + l32, logical chunk 2 kk + half
@@ -671,8 +691,28 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
                                         it.w, nchunk);
                 }
             }
+#ifdef BSA_TRACE
+            tr_last = __builtin_amdgcn_s_memrealtime();
+            ++tr_items;
+            tr_blocks += it.z - it.y;
+#endif
         }
     }
+#ifdef BSA_TRACE
+    if (t == 0 && blockIdx.x < kTraceMax) {
+        TraceRec r;
+        r.t0 = tr_t0;
+        r.t_last = tr_last;
+        r.t_end = __builtin_amdgcn_s_memrealtime();
+        r.c0 = tr_c0;
+        r.c_end = __builtin_amdgcn_s_memtime();
+        r.hw_id = __builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));   // HW_REG_HW_ID
+        r.xcc = (uint32_t)xcc_id();
+        r.items = tr_items;
+        r.blocks = tr_blocks;
+        g_trace_rec[blockIdx.x] = r;
+    }
+#endif
 }
 
 template <int D, int B>
@@ -756,3 +796,15 @@ int attn_max_heads() { return kMaxHeads; }
 int attn_max_blocks() { return kMaxBlocks; }
 
 }  // namespace bsa
+
+#ifdef BSA_TRACE
+// Copy the first `count` workgroup records of the latest attention launch (56 bytes each:
+// t0, t_last, t_end as uint64 s_memrealtime ticks, c0, c_end as uint64 s_memtime ticks, hw_id,
+// xcc as uint32, items, blocks as int32) to host memory.  Synchronous; debug builds only.
+extern "C" BSA_API int bsa_trace_read(void* host, int32_t count) {
+    if (!host || count < 0 || count > bsa::kTraceMax) return -1;
+    return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(bsa::g_trace_rec),
+                                    (size_t)count * sizeof(bsa::TraceRec), 0,
+                                    hipMemcpyDeviceToHost);
+}
+#endif

@@ -38,6 +38,11 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Every entry point below is exported from libbsa.so; the library's other symbols are hidden. */
+#ifndef BSA_API
+#define BSA_API __attribute__((visibility("default")))
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -66,8 +71,8 @@ typedef struct {
 
 /* ---- host-only helpers ------------------------------------------------------------- */
 /* ceil(N / block) and n_blk * block; 0 for an invalid grid. */
-int32_t bsa_num_blocks(const bsa_grid* grid);
-int32_t bsa_padded_len(const bsa_grid* grid);
+BSA_API int32_t bsa_num_blocks(const bsa_grid* grid);
+BSA_API int32_t bsa_padded_len(const bsa_grid* grid);
 
 /* ---- 1. video-aware block organization (FVAttn abstract) --------------------------- */
 /* inverse == 0: src raster bf16 [batch, N, heads, D] -> dst tiled bf16 [batch, heads, Npad, D];
@@ -75,12 +80,12 @@ int32_t bsa_padded_len(const bsa_grid* grid);
  * inverse != 0: src tiled [batch, heads, Npad, D] -> dst raster [batch, N, heads, D]; pad rows
  *               of src are not read.
  * src and dst must not overlap.  Supported head_dim: any multiple of 8 in [8, 1024]. */
-bsa_status bsa_reorder(const void* src, void* dst, const bsa_shape* shape,
+BSA_API bsa_status bsa_reorder(const void* src, void* dst, const bsa_shape* shape,
                        const bsa_grid* grid, int32_t inverse, void* stream);
 
 /* ---- 2. routing frontend: pooled block scores, Top-p with a Top-k floor (FVAttn) ---- */
 /* Workspace bytes bsa_score_and_route needs (depends on shape and grid only). */
-size_t bsa_route_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid);
+BSA_API size_t bsa_route_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid);
 
 /* For every row (b, h, i):
  *   qbar_i, kbar_j = means of the tiled Q and K over the real tokens of block i / j (fp64),
@@ -97,7 +102,7 @@ size_t bsa_route_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid);
  * Errors: top_p NaN or outside [0, 1], k_floor < 1, scale not finite -> BSA_ERR_INVALID_ARG;
  * rows*n_blk must fit int32; n_blk <= 4096.
  * ws: device workspace of at least bsa_route_workspace_bytes() bytes, 256-byte aligned. */
-bsa_status bsa_score_and_route(const void* q_t, const void* k_t, const bsa_shape* shape,
+BSA_API bsa_status bsa_score_and_route(const void* q_t, const void* k_t, const bsa_shape* shape,
                                const bsa_grid* grid, double top_p, int32_t k_floor,
                                double scale, int32_t* row_ptr, int32_t* col_idx,
                                int32_t* nnz, double* block_scores, void* ws,
@@ -106,7 +111,7 @@ bsa_status bsa_score_and_route(const void* q_t, const void* k_t, const bsa_shape
 /* ---- 3. exact block-sparse attention (online softmax over the kept blocks) --------- */
 /* Workspace bytes bsa_sparse_attn_fwd needs: worst case over every possible CSR, so the host
  * never needs nnz. */
-size_t bsa_attn_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid);
+BSA_API size_t bsa_attn_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid);
 
 /* For every real query position p of block i in row r = (b, h, i):
  *   U = real key positions of the blocks col_idx[row_ptr[r] .. row_ptr[r+1]),
@@ -123,7 +128,7 @@ size_t bsa_attn_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid);
  * lengths, long rows are split and their partial results merged in a fixed order, so the
  * output is bitwise deterministic.
  * ws: device workspace of at least bsa_attn_workspace_bytes() bytes, 256-byte aligned. */
-bsa_status bsa_sparse_attn_fwd(const void* q_t, const void* k_t, const void* v_t,
+BSA_API bsa_status bsa_sparse_attn_fwd(const void* q_t, const void* k_t, const void* v_t,
                                const int32_t* row_ptr, const int32_t* col_idx,
                                const bsa_shape* shape, const bsa_grid* grid, float scale,
                                void* out_t, float* lse, void* ws, size_t ws_bytes,
@@ -132,8 +137,8 @@ bsa_status bsa_sparse_attn_fwd(const void* q_t, const void* k_t, const void* v_t
 /* ---- diagnostics ------------------------------------------------------------------- */
 /* Message of the calling thread's last non-OK status ("" if none).  Valid until the next
  * call on the same thread. */
-const char* bsa_last_error(void);
-const char* bsa_version(void);
+BSA_API const char* bsa_last_error(void);
+BSA_API const char* bsa_version(void);
 
 #ifdef __cplusplus
 }

@@ -40,6 +40,19 @@ def test_library_exports_every_declared_symbol():
     exported = set(re.findall(r"\bT (bsa_\w+)", r.stdout))
     assert set(names) <= exported
     assert exported <= set(names), exported - set(names)     # nothing undeclared leaks
+    # no C++ symbol of the implementation is exported either
+    assert not re.search(r"\bT _Z", r.stdout), re.findall(r"\bT (_Z\w+)", r.stdout)[:5]
+
+
+def test_trace_library_adds_only_the_trace_reader():
+    """libbsa_trace.so (the -DBSA_TRACE debug build) exports the same ABI plus
+    bsa_trace_read; the product library does not contain it."""
+    assert os.path.exists(bsa.TRACE_LIB_PATH)
+    r = subprocess.run(["nm", "-D", "--defined-only", bsa.TRACE_LIB_PATH], capture_output=True,
+                       text=True)
+    exported = set(re.findall(r"\bT (bsa_\w+)", r.stdout))
+    assert exported == set(_declared()) | {"bsa_trace_read"}
+    assert not hasattr(ctypes.CDLL(bsa.LIB_PATH), "bsa_trace_read")
 
 
 def test_version_and_geometry_helpers():
