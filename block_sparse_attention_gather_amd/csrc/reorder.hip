@@ -19,75 +19,98 @@ struct GridArgs {
     int32_t T, H, W, tt, th, tw;
 };
 
-__device__ __forceinline__ int64_t tile_pos_to_raster(int64_t p, const GridArgs& g) {
-    const int64_t slab = (int64_t)g.tt * g.H * g.W;
-    const int64_t it = p / slab;
-    int64_t r = p - it * slab;
-    const int64_t et = min((int64_t)g.tt, (int64_t)g.T - it * g.tt);
-    const int64_t row = et * g.th * g.W;
-    const int64_t ih = r / row;
+// Tile-order position p -> raster token n, in 32-bit arithmetic (N < 2^31 is checked on the
+// host, so every intermediate fits).
+__device__ __forceinline__ uint32_t tile_pos_to_raster(uint32_t p, const GridArgs& g) {
+    const uint32_t T = g.T, H = g.H, W = g.W, tt = g.tt, th = g.th, tw = g.tw;
+    const uint32_t slab = tt * H * W;
+    const uint32_t it = p / slab;
+    uint32_t r = p - it * slab;
+    const uint32_t et = min(tt, T - it * tt);
+    const uint32_t row = et * th * W;
+    const uint32_t ih = r / row;
     r -= ih * row;
-    const int64_t eh = min((int64_t)g.th, (int64_t)g.H - ih * g.th);
-    const int64_t tile = et * eh * g.tw;
-    const int64_t iw = r / tile;
+    const uint32_t eh = min(th, H - ih * th);
+    const uint32_t tile = et * eh * tw;
+    const uint32_t iw = r / tile;
     r -= iw * tile;
-    const int64_t ew = min((int64_t)g.tw, (int64_t)g.W - iw * g.tw);
-    const int64_t rt = r / (eh * ew);
-    r -= rt * eh * ew;
-    const int64_t rh = r / ew;
-    const int64_t rw = r - rh * ew;
-    const int64_t t = it * g.tt + rt, h = ih * g.th + rh, w = iw * g.tw + rw;
-    return (t * g.H + h) * g.W + w;
+    const uint32_t ew = min(tw, W - iw * tw);
+    const uint32_t plane = eh * ew;
+    const uint32_t rt = r / plane;
+    r -= rt * plane;
+    const uint32_t rh = r / ew;
+    const uint32_t rw = r - rh * ew;
+    const uint32_t t = it * tt + rt, h = ih * th + rh, w = iw * tw + rw;
+    return (t * H + h) * W + w;
 }
 
 constexpr int kReorderThreads = 256;
-constexpr int kUnroll = 4;
 
-// One wavefront per (batch, tile position).  chunks = heads * D / 8 (16-byte chunks).
+// One wavefront per tile position p of batch blockIdx.y moves one token: the heads * D
+// contiguous raster elements <-> `heads` rows of D elements in the tiled layout, as 16-byte
+// chunks (chunk c = head c / DCH, column chunk c % DCH).  DCH = D / 8 is a compile-time
+// constant for D = 64 and 128 (0 = runtime dch for other head sizes).  Forward (INV = false)
+// writes zeros to the pad positions p >= N; inverse reads only real positions.  Each lane
+// keeps up to U chunks in flight before it stores them.  All index math is 32-bit except the
+// element offsets, and the batch index is blockIdx.y, so no 64-bit division is left.
+template <int DCH, int U, bool INV>
 __global__ __launch_bounds__(kReorderThreads) void reorder_kernel(
-    const uint4* __restrict__ src, uint4* __restrict__ dst, GridArgs g, int32_t batch,
-    int32_t heads, int32_t dch, int64_t N, int64_t Npad, int inverse) {
+    const uint4* __restrict__ src, uint4* __restrict__ dst, GridArgs g, int32_t heads,
+    int32_t dch_rt, uint32_t N, uint32_t Npad) {
+    const int dch = DCH ? DCH : dch_rt;
     const int lane = threadIdx.x & 63;
-    const int64_t wave = ((int64_t)blockIdx.x * kReorderThreads + threadIdx.x) >> 6;
-    const int64_t nwaves = ((int64_t)gridDim.x * kReorderThreads) >> 6;
-    const int64_t npos = inverse ? N : Npad;
+    const uint32_t wave = (blockIdx.x * kReorderThreads + threadIdx.x) >> 6;
+    const uint32_t nwaves = (gridDim.x * kReorderThreads) >> 6;
+    const uint32_t npos = INV ? N : Npad;
     const int32_t chunks = heads * dch;
-    for (int64_t w = wave; w < (int64_t)batch * npos; w += nwaves) {
-        const int64_t b = w / npos;
-        const int64_t p = w - b * npos;
-        const bool real = p < N;
-        const int64_t n = real ? tile_pos_to_raster(p, g) : 0;
-        const int64_t raster_base = (b * N + n) * (int64_t)chunks;      // in chunks
-        const int64_t tiled_head0 = (b * heads * Npad + p) * (int64_t)dch;
-        const int64_t head_stride = Npad * (int64_t)dch;
-        for (int32_t c0 = lane; c0 < chunks; c0 += 64 * kUnroll) {
-            uint4 v[kUnroll];
-            int64_t toff[kUnroll];
+    const int64_t b = blockIdx.y;
+    const int64_t head_stride = (int64_t)Npad * dch;
+    for (uint32_t p = wave; p < npos; p += nwaves) {
+        const bool real = INV || p < N;
+        const uint32_t n = real ? tile_pos_to_raster(p, g) : 0u;
+        const uint4* rs = (INV ? dst : src) + (b * N + n) * (int64_t)chunks;   // raster row
+        const int64_t tiled0 = (b * heads * (int64_t)Npad + p) * (int64_t)dch;
+        for (int32_t c0 = lane; c0 < chunks; c0 += 64 * U) {
+            uint4 v[U];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
+            for (int u = 0; u < U; ++u) {
                 const int32_t c = c0 + 64 * u;
-                const int32_t h = c / dch;
-                const int32_t dc = c - h * dch;
-                toff[u] = tiled_head0 + h * head_stride + dc;
                 if (c < chunks) {
-                    if (!inverse)
-                        v[u] = real ? src[raster_base + c] : make_uint4(0, 0, 0, 0);
+                    const int32_t h = c / dch;
+                    const int64_t toff = tiled0 + h * head_stride + (c - h * dch);
+                    if (INV)
+                        v[u] = src[toff];
                     else
-                        v[u] = src[toff[u]];
+                        v[u] = real ? rs[c] : make_uint4(0, 0, 0, 0);
                 }
             }
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
+            for (int u = 0; u < U; ++u) {
                 const int32_t c = c0 + 64 * u;
                 if (c < chunks) {
-                    if (!inverse)
-                        dst[toff[u]] = v[u];
+                    const int32_t h = c / dch;
+                    const int64_t toff = tiled0 + h * head_stride + (c - h * dch);
+                    if (INV)
+                        dst[(b * N + n) * (int64_t)chunks + c] = v[u];
                     else
-                        dst[raster_base + c] = v[u];
+                        dst[toff] = v[u];
                 }
             }
         }
     }
+}
+
+// Chunks in flight per lane: 4 forward, 2 inverse (inverse reads 256-byte rows of `heads`
+// different tiled rows; more than two per lane measured slower).
+template <int DCH>
+void launch_dir(const uint4* sp, uint4* dp, const GridArgs& ga, dim3 grid, int32_t heads,
+                int32_t dch, uint32_t N, uint32_t Npad, int inverse, hipStream_t s) {
+    if (inverse)
+        hipLaunchKernelGGL((reorder_kernel<DCH, 2, true>), grid, dim3(kReorderThreads), 0, s, sp,
+                           dp, ga, heads, dch, N, Npad);
+    else
+        hipLaunchKernelGGL((reorder_kernel<DCH, 4, false>), grid, dim3(kReorderThreads), 0, s,
+                           sp, dp, ga, heads, dch, N, Npad);
 }
 
 }  // namespace
@@ -95,14 +118,21 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_kernel(
 bsa_status launch_reorder(const void* src, void* dst, int32_t batch, int32_t heads, int32_t D,
                           const Geometry& g, int inverse, hipStream_t s) {
     GridArgs ga{g.T, g.H, g.W, g.tt, g.th, g.tw};
-    const int64_t npos = (int64_t)batch * (inverse ? g.N : g.Npad);
-    if (npos == 0) return BSA_OK;
+    const int64_t npos = inverse ? g.N : g.Npad;
+    if (npos == 0 || batch == 0) return BSA_OK;
     const int64_t waves_per_block = kReorderThreads / 64;
     int64_t blocks = (npos + waves_per_block - 1) / waves_per_block;
     blocks = blocks > 65536 ? 65536 : blocks;
-    hipLaunchKernelGGL(reorder_kernel, dim3((unsigned)blocks), dim3(kReorderThreads), 0, s,
-                       (const uint4*)src, (uint4*)dst, ga, batch, heads, D / 8, g.N, g.Npad,
-                       inverse);
+    const dim3 grid((unsigned)blocks, (unsigned)batch);
+    const uint4* sp = (const uint4*)src;
+    uint4* dp = (uint4*)dst;
+    const uint32_t N = (uint32_t)g.N, Npad = (uint32_t)g.Npad;
+    if (D == 128)
+        launch_dir<16>(sp, dp, ga, grid, heads, 16, N, Npad, inverse, s);
+    else if (D == 64)
+        launch_dir<8>(sp, dp, ga, grid, heads, 8, N, Npad, inverse, s);
+    else
+        launch_dir<0>(sp, dp, ga, grid, heads, D / 8, N, Npad, inverse, s);
     return check_launch("reorder");
 }
 

@@ -245,6 +245,258 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
     }
 }
 
+
+// ---------------------------------------------------------------------------------------
+// score: S[bh][i][j] = scale * <qbar_i, kbar_j>, fp64 MFMA 16x16x4 (rows of up to 2048 blocks).
+// 1-D grid of 8 * T * ceil(bh / 8) workgroups, T = ceil(n/64)^2 tiles of 64 x 64 per head:
+// workgroup L runs on XCD L % 8 and takes tile (L / 8) % T of head L % 8 + 8 (L / 8 / T), so
+// each head's pooled rows are fetched into one XCD's L2.  Wave (wr, wc) owns the 32 x 32
+// sub-tile at (32 wr, 32 wc) as 2 x 2 MFMA tiles.  In MFMA step t the k-slot ks = lane / 16
+// carries feature d = ks D/4 + t, so each lane streams a contiguous quarter of its row.
+// ---------------------------------------------------------------------------------------
+typedef double dbl4 __attribute__((ext_vector_type(4)));
+
+template <int D>
+__global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ qbar,
+                                                    const double* __restrict__ kbar,
+                                                    double* __restrict__ S, double scale,
+                                                    int32_t n, int32_t bh, int32_t tiles) {
+    constexpr int Q4 = D / 4;
+    const uint32_t L = blockIdx.x;
+    const uint32_t T = (uint32_t)tiles * tiles;
+    const uint32_t k = L >> 3;
+    const uint32_t h = (L & 7) + 8 * (k / T);
+    if (h >= (uint32_t)bh) return;
+    const uint32_t tile = k % T;
+    const int ti = tile / tiles, tj = tile - ti * tiles;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int ks = lane >> 4, sub = lane & 15;
+    const int row0 = ti * 64 + (w >> 1) * 32;
+    const int col0 = tj * 64 + (w & 1) * 32;
+    const double* pa[2];
+    const double* pb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int r = min(row0 + 16 * u + sub, n - 1);      // rows past n: computed, not stored
+        const int c = min(col0 + 16 * u + sub, n - 1);
+        pa[u] = qbar + ((size_t)h * n + r) * D + ks * Q4;
+        pb[u] = kbar + ((size_t)h * n + c) * D + ks * Q4;
+    }
+    dbl4 acc[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int v = 0; v < 2; ++v) acc[u][v] = dbl4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 2
+    for (int t0 = 0; t0 < Q4; t0 += 4) {
+        double2 av[2][2], bv[2][2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            av[u][0] = *(const double2*)(pa[u] + t0);
+            av[u][1] = *(const double2*)(pa[u] + t0 + 2);
+            bv[u][0] = *(const double2*)(pb[u] + t0);
+            bv[u][1] = *(const double2*)(pb[u] + t0 + 2);
+        }
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int v = 0; v < 2; ++v) {
+                    const double x = (st & 1) ? av[u][st >> 1].y : av[u][st >> 1].x;
+                    const double y = (st & 1) ? bv[v][st >> 1].y : bv[v][st >> 1].x;
+                    acc[u][v] = __builtin_amdgcn_mfma_f64_16x16x4f64(x, y, acc[u][v], 0, 0, 0);
+                }
+    }
+    // accumulator element e of a lane holds tile row 4 e + ks, tile column sub
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            const int j = col0 + 16 * v + sub;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = row0 + 16 * u + 4 * e + ks;
+                if (i < n && j < n) S[((size_t)h * n + i) * n + j] = scale * acc[u][v][e];
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------------------
+// route_sort: one wavefront per row (n_blk <= 2048), four rows per workgroup, no barriers.
+// Lane l holds sorted positions e = EPL l + r, r < EPL (64 EPL = P2 >= n_blk).  Each block is
+// one 64-bit word: the order key of its score (ascending key = descending score) with the
+// low log2(P2) bits replaced by the block index, so the words are distinct and ascending
+// word order is descending score with ties, down to 2^-(52 - log2 P2) relative, going to the
+// smaller index.  Bitonic network: distances below EPL swap registers, the others exchange
+// lanes (DPP within a row of 16, permlane swaps across rows and halves).  Then the exact
+// scores are gathered in sorted order for the block mass, its prefix, the cut and the bitmap.
+// ---------------------------------------------------------------------------------------
+constexpr int kSortRows = 4;                   // wavefronts (rows) per workgroup
+constexpr int kSortMaxWords = 64;              // bitmap words per row, n_blk <= 2048
+
+struct SortArgs {
+    const double* scores;   // [rows][n]
+    uint32_t* bitmap;       // [rows][nwords]
+    int32_t* counts;        // [rows]
+    double top_p;
+    int32_t k_floor;
+    int32_t n_blk;
+    int32_t nwords;
+    int64_t rows;
+};
+
+// value of lane (l ^ M) for a lane distance M in {1, 2, 4, 8, 16, 32}
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+    const int x = (int)v;
+    if constexpr (M == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);   // quad [1,0,3,2]
+    } else if constexpr (M == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);   // quad [2,3,0,1]
+    } else if constexpr (M == 4) {
+        // mirror within 8 lanes (i -> 7 - i), then quad [3,2,1,0] (i -> i ^ 3): i -> i ^ 4
+        const int y = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);
+        return (uint32_t)__builtin_amdgcn_mov_dpp(y, 0x1B, 0xF, 0xF, false);
+    } else if constexpr (M == 8) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // rotate row by 8
+    } else if constexpr (M == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (threadIdx.x & 16) ? r[0] : r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (threadIdx.x & 32) ? r[0] : r[1];
+    }
+}
+
+template <int M>
+__device__ __forceinline__ uint64_t lane_xor64(uint64_t v) {
+    const uint32_t lo = lane_xor<M>((uint32_t)v);
+    const uint32_t hi = lane_xor<M>((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// one pass (block size KK, distance JJ) of the ascending bitonic network, then the passes of
+// the smaller distances
+template <int EPL, int KK, int JJ>
+__device__ __forceinline__ void bitonic_passes(uint64_t (&key)[EPL], int lane) {
+    if constexpr (JJ < EPL) {
+#pragma unroll
+        for (int r = 0; r < EPL; ++r) {
+            if (r & JJ) continue;
+            const int rp = r | JJ;
+            const bool up = KK < EPL ? (r & KK) == 0 : (lane & (KK / EPL)) == 0;
+            const bool sw = (key[r] > key[rp]) == up;
+            const uint64_t a = key[r], b = key[rp];
+            key[r] = sw ? b : a;
+            key[rp] = sw ? a : b;
+        }
+    } else {
+        constexpr int M = JJ / EPL;
+        const bool wmax = ((lane & M) == 0) != ((lane & (KK / EPL)) == 0);
+#pragma unroll
+        for (int r = 0; r < EPL; ++r) {
+            const uint64_t p = lane_xor64<M>(key[r]);
+            key[r] = ((key[r] > p) != wmax) ? p : key[r];
+        }
+    }
+    if constexpr (JJ > 1) bitonic_passes<EPL, KK, JJ / 2>(key, lane);
+}
+
+template <int EPL, int KK>
+__device__ __forceinline__ void bitonic_sort(uint64_t (&key)[EPL], int lane) {
+    bitonic_passes<EPL, KK, KK / 2>(key, lane);
+    if constexpr (KK < 64 * EPL) bitonic_sort<EPL, 2 * KK>(key, lane);
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+template <int EPL>
+__global__ __launch_bounds__(kSortRows * 64) void route_sort_kernel(SortArgs a) {
+    constexpr int IB = 6 + (EPL >= 2) + (EPL >= 4) + (EPL >= 8) + (EPL >= 16) + (EPL >= 32);
+    constexpr uint64_t IM = (1ull << IB) - 1;
+    __shared__ uint32_t bits[kSortRows][kSortMaxWords];
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int64_t row = (int64_t)blockIdx.x * kSortRows + w;
+    if (row >= a.rows) return;
+    const int n = a.n_blk;
+    const double* srow = a.scores + row * n;
+    for (int q = lane; q < a.nwords; q += 64) bits[w][q] = 0u;
+
+    uint64_t key[EPL];
+#pragma unroll
+    for (int r = 0; r < EPL; ++r) {
+        const int e = EPL * lane + r;
+        key[r] = e < n ? (desc_key(srow[e]) & ~IM) | (uint64_t)e : ~0ull;
+    }
+    bitonic_sort<EPL, 2>(key, lane);
+
+    // exact scores in sorted order; position 0 (lane 0, r 0) holds the row maximum
+    double m[EPL];
+#pragma unroll
+    for (int r = 0; r < EPL; ++r) {
+        const int e = EPL * lane + r;
+        m[r] = e < n ? srow[key[r] & IM] : 0.0;
+    }
+    const uint64_t mb = (uint64_t)__double_as_longlong(m[0]);
+    const uint32_t mlo = __builtin_amdgcn_readfirstlane((uint32_t)mb);
+    const uint32_t mhi = __builtin_amdgcn_readfirstlane((uint32_t)(mb >> 32));
+    const double smax = __longlong_as_double((long long)(((uint64_t)mhi << 32) | mlo));
+    double local = 0.0;
+#pragma unroll
+    for (int r = 0; r < EPL; ++r) {
+        const int e = EPL * lane + r;
+        m[r] = e < n ? exp(m[r] - smax) : 0.0;
+        local += m[r];
+    }
+    const double Z = wave_sum(local);
+    double run = 0.0;
+#pragma unroll
+    for (int r = 0; r < EPL; ++r) {
+        m[r] = m[r] / Z;
+        run += m[r];
+    }
+    // exclusive prefix of the lane totals
+    double incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double u = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += u;
+    }
+    double cum = incl - run;
+    int first = n;                                     // first position with cum >= top_p
+#pragma unroll
+    for (int r = 0; r < EPL; ++r) {
+        const int e = EPL * lane + r;
+        cum += m[r];
+        if (first == n && e < n && cum >= a.top_p) first = e;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) first = min(first, __shfl_xor(first, off, 64));
+    int kp;
+    if (a.top_p >= 1.0) kp = n;
+    else if (a.top_p <= 0.0) kp = 0;
+    else kp = first < n ? first + 1 : n;
+    const int c = min(n, max(kp, a.k_floor));
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // zeroed words, then bit sets
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int r = 0; r < EPL; ++r) {
+        const int e = EPL * lane + r;
+        const uint32_t j = (uint32_t)(key[r] & IM);
+        if (e < c) atomicOr(&bits[w][j >> 5], 1u << (j & 31));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // bit sets, then reads
+    __builtin_amdgcn_wave_barrier();
+    for (int q = lane; q < a.nwords; q += 64) a.bitmap[row * a.nwords + q] = bits[w][q];
+    if (lane == 0) a.counts[row] = c;
+}
+
 // ---------------------------------------------------------------------------------------
 // scan: one workgroup; counts -> row_ptr (exclusive, rows + 1 entries) and nnz
 // ---------------------------------------------------------------------------------------
@@ -312,7 +564,7 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(const uint32_t* __restri
 }
 
 struct RouteLayout {
-    size_t qbar, kbar, bitmap, counts, total;
+    size_t qbar, kbar, bitmap, counts, scores, total;
 };
 
 RouteLayout route_layout(int32_t batch, int32_t heads, int32_t D, const Geometry& g) {
@@ -325,6 +577,8 @@ RouteLayout route_layout(int32_t batch, int32_t heads, int32_t D, const Geometry
     L.kbar = off;   off = align_up(off + bh * g.n_blk * D * 8, 256);
     L.bitmap = off; off = align_up(off + rows * nwords * 4, 256);
     L.counts = off; off = align_up(off + rows * 4, 256);
+    L.scores = off;
+    if (g.n_blk <= kSortMaxWords * 32) off = align_up(off + rows * (size_t)g.n_blk * 8, 256);
     L.total = off;
     return L;
 }
@@ -376,16 +630,52 @@ bsa_status launch_route(const void* q_t, const void* k_t, int32_t batch, int32_t
     R = R < 1 ? 1 : (R > 8 ? 8 : R);
     a.R = R;
     a.nwords = (g.n_blk + 31) / 32;
-    const size_t lds = route_lds_bytes(D, P2, R) + 16;
-    dim3 rgrid((g.n_blk + R - 1) / R, bh);
-    if (D == 64) {
-        (void)hipFuncSetAttribute((const void*)route_kernel<64>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        hipLaunchKernelGGL(route_kernel<64>, rgrid, dim3(kThreads), lds, s, a);
+    if (g.n_blk <= kSortMaxWords * 32) {
+        // scores by MFMA into block_scores (or the workspace), then one wavefront per row
+        double* S = block_scores ? block_scores : (double*)(w + L.scores);
+        const int tiles = (g.n_blk + 63) / 64;
+        const unsigned sgrid = 8u * (unsigned)(tiles * tiles) * (unsigned)((bh + 7) / 8);
+        if (D == 64)
+            hipLaunchKernelGGL(score_kernel<64>, dim3(sgrid), dim3(256), 0, s, qbar, kbar, S,
+                               scale, g.n_blk, bh, tiles);
+        else
+            hipLaunchKernelGGL(score_kernel<128>, dim3(sgrid), dim3(256), 0, s, qbar, kbar, S,
+                               scale, g.n_blk, bh, tiles);
+        st = check_launch("score");
+        if (st != BSA_OK) return st;
+        SortArgs sa;
+        sa.scores = S;
+        sa.bitmap = bitmap;
+        sa.counts = counts;
+        sa.top_p = top_p;
+        sa.k_floor = k_floor;
+        sa.n_blk = g.n_blk;
+        sa.nwords = a.nwords;
+        sa.rows = rows;
+        const dim3 ogrid((unsigned)((rows + kSortRows - 1) / kSortRows));
+        const dim3 oblk(kSortRows * 64);
+        const int epl = P2 <= 64 ? 1 : P2 / 64;
+        switch (epl) {
+            case 1:  hipLaunchKernelGGL(route_sort_kernel<1>, ogrid, oblk, 0, s, sa); break;
+            case 2:  hipLaunchKernelGGL(route_sort_kernel<2>, ogrid, oblk, 0, s, sa); break;
+            case 4:  hipLaunchKernelGGL(route_sort_kernel<4>, ogrid, oblk, 0, s, sa); break;
+            case 8:  hipLaunchKernelGGL(route_sort_kernel<8>, ogrid, oblk, 0, s, sa); break;
+            case 16: hipLaunchKernelGGL(route_sort_kernel<16>, ogrid, oblk, 0, s, sa); break;
+            default: hipLaunchKernelGGL(route_sort_kernel<32>, ogrid, oblk, 0, s, sa); break;
+        }
     } else {
-        (void)hipFuncSetAttribute((const void*)route_kernel<128>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        hipLaunchKernelGGL(route_kernel<128>, rgrid, dim3(kThreads), lds, s, a);
+        // longer rows: one workgroup scores and sorts R rows in LDS
+        const size_t lds = route_lds_bytes(D, a.P2, R) + 16;
+        dim3 rgrid((g.n_blk + R - 1) / R, bh);
+        if (D == 64) {
+            (void)hipFuncSetAttribute((const void*)route_kernel<64>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            hipLaunchKernelGGL(route_kernel<64>, rgrid, dim3(kThreads), lds, s, a);
+        } else {
+            (void)hipFuncSetAttribute((const void*)route_kernel<128>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            hipLaunchKernelGGL(route_kernel<128>, rgrid, dim3(kThreads), lds, s, a);
+        }
     }
     st = check_launch("route");
     if (st != BSA_OK) return st;

@@ -145,3 +145,20 @@ def test_attention_on_given_csr(D, B, heads, grid3, tile, kinds, seed):
     dl = np.abs(lse.cpu().numpy().astype(np.float64)[:, :, :N] - Lref[:, :, :N])
     assert dl.max() <= 1e-3
     assert np.all(bf16_f64(out_t)[:, :, N:] == 0)
+
+
+@pytest.mark.parametrize("D", [8, 64, 128, 136])
+def test_reorder_batched_any_head_dim(D):
+    """Both directions bit-exact for batch 3, a ragged grid with truncated tiles on every axis,
+    and head sizes on the compile-time (64, 128) and runtime (8, 136) paths."""
+    T, H, W, tile, B, heads, batch = 3, 10, 13, (2, 4, 4), 64, 3, 3
+    rng = np.random.default_rng(40 + D)
+    N = T * H * W
+    x = rng.integers(0, 1 << 16, size=(batch, N, heads, D), dtype=np.uint16)
+    grid = bsa.Grid(T, H, W, tile, B)
+    print(f"[gpu] reorder batch={batch} N={N} heads={heads} D={D}", flush=True)
+    xt = bsa.reorder(to_dev(x), grid)
+    ref = O.reorder(x, T, H, W, tile, B)
+    assert np.array_equal(to_bits(xt), ref)
+    back = bsa.reorder(xt, grid, inverse=True)
+    assert np.array_equal(to_bits(back), x)
