@@ -88,8 +88,10 @@ def _load():
         "bsa_num_blocks": (I32, [G]),
         "bsa_padded_len": (I32, [G]),
         "bsa_reorder": (I32, [P, P, S, G, I32, P]),
+        "bsa_reorder_pool": (I32, [P, P, P, S, G, P]),
         "bsa_route_workspace_bytes": (SZ, [S, G]),
         "bsa_score_and_route": (I32, [P, P, S, G, F64, I32, F64, P, P, P, P, P, SZ, P]),
+        "bsa_route_pooled": (I32, [P, P, S, G, F64, I32, F64, P, P, P, P, P, SZ, P]),
         "bsa_attn_workspace_bytes": (SZ, [S, G]),
         "bsa_sparse_attn_fwd": (I32, [P, P, P, P, P, S, G, F32, P, P, P, SZ, P]),
         "bsa_last_error": (ctypes.c_char_p, []),
@@ -201,6 +203,30 @@ def reorder(x, grid: Grid, inverse: bool = False, out=None):
     return out
 
 
+def reorder_pool(x, grid: Grid, out=None, pooled=None):
+    """Forward reorder plus the per-block means routing pools: raster [b, N, h, D] bf16 ->
+    (tiled [b, h, Npad, D] bf16, pooled [b, h, n_blk, D] fp64), in one pass over x."""
+    import torch
+    _require(x, torch.bfloat16, "x")
+    b, N, h, D = x.shape
+    if N != grid.N:
+        raise ValueError(f"x has {N} tokens, grid has {grid.N}")
+    if out is None:
+        out = torch.empty((b, h, grid.Npad, D), dtype=x.dtype, device=x.device)
+    _require(out, torch.bfloat16, "out")
+    if tuple(out.shape) != (b, h, grid.Npad, D):
+        raise ValueError(f"out must have shape {(b, h, grid.Npad, D)}")
+    if pooled is None:
+        pooled = torch.empty((b, h, grid.n_blk, D), dtype=torch.float64, device=x.device)
+    _require(pooled, torch.float64, "pooled")
+    if tuple(pooled.shape) != (b, h, grid.n_blk, D):
+        raise ValueError(f"pooled must have shape {(b, h, grid.n_blk, D)}")
+    g, s = grid._c(), _shape(b, h, D)
+    _check(_load().bsa_reorder_pool(x.data_ptr(), out.data_ptr(), pooled.data_ptr(),
+                                    ctypes.byref(s), ctypes.byref(g), _stream(x)))
+    return out, pooled
+
+
 def route_workspace_bytes(batch, heads, D, grid: Grid) -> int:
     g, s = grid._c(), _shape(batch, heads, D)
     return int(_load().bsa_route_workspace_bytes(ctypes.byref(s), ctypes.byref(g)))
@@ -214,21 +240,8 @@ def attn_workspace_bytes(batch, heads, D, grid: Grid) -> int:
     return n
 
 
-def score_and_route(q_t, k_t, grid: Grid, top_p: float, k_floor: int,
-                    scale: Optional[float] = None, return_scores: bool = False,
-                    workspace=None, row_ptr=None, col_idx=None, nnz=None):
-    """Pooled block scores and Top-p / Top-k routing -> (row_ptr, col_idx, nnz[, scores]).
-
-    col_idx has the worst-case capacity rows * n_blk; its first nnz entries are the CSR
-    columns.  nnz stays on the device (a 1-element int32 tensor)."""
+def _route_outputs(b, h, D, grid, dev, return_scores, workspace, row_ptr, col_idx, nnz):
     import torch
-    _require(q_t, torch.bfloat16, "q_t")
-    _require(k_t, torch.bfloat16, "k_t")
-    b, h, Np, D = q_t.shape
-    if tuple(k_t.shape) != (b, h, Np, D) or Np != grid.Npad:
-        raise ValueError("q_t/k_t must both be [b, h, Npad, D] for this grid")
-    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    dev = q_t.device
     rows = b * h * grid.n_blk
     if row_ptr is None:
         row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
@@ -246,11 +259,54 @@ def score_and_route(q_t, k_t, grid: Grid, top_p: float, k_floor: int,
     need = route_workspace_bytes(b, h, D, grid)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    return scores, workspace, row_ptr, col_idx, nnz
+
+
+def score_and_route(q_t, k_t, grid: Grid, top_p: float, k_floor: int,
+                    scale: Optional[float] = None, return_scores: bool = False,
+                    workspace=None, row_ptr=None, col_idx=None, nnz=None):
+    """Pooled block scores and Top-p / Top-k routing -> (row_ptr, col_idx, nnz[, scores]).
+
+    col_idx has the worst-case capacity rows * n_blk; its first nnz entries are the CSR
+    columns.  nnz stays on the device (a 1-element int32 tensor)."""
+    import torch
+    _require(q_t, torch.bfloat16, "q_t")
+    _require(k_t, torch.bfloat16, "k_t")
+    b, h, Np, D = q_t.shape
+    if tuple(k_t.shape) != (b, h, Np, D) or Np != grid.Npad:
+        raise ValueError("q_t/k_t must both be [b, h, Npad, D] for this grid")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    scores, workspace, row_ptr, col_idx, nnz = _route_outputs(
+        b, h, D, grid, q_t.device, return_scores, workspace, row_ptr, col_idx, nnz)
     g, s = grid._c(), _shape(b, h, D)
     _check(_load().bsa_score_and_route(
         q_t.data_ptr(), k_t.data_ptr(), ctypes.byref(s), ctypes.byref(g), float(top_p),
         int(k_floor), scale, row_ptr.data_ptr(), col_idx.data_ptr(), nnz.data_ptr(),
         _ptr(scores), workspace.data_ptr(), workspace.numel(), _stream(q_t)))
+    if return_scores:
+        return row_ptr, col_idx, nnz, scores
+    return row_ptr, col_idx, nnz
+
+
+def route_pooled(qbar, kbar, grid: Grid, top_p: float, k_floor: int,
+                 scale: Optional[float] = None, return_scores: bool = False,
+                 workspace=None, row_ptr=None, col_idx=None, nnz=None):
+    """score_and_route from the block means reorder_pool returns ([b, h, n_blk, D] fp64);
+    same outputs as score_and_route on the tiled Q and K."""
+    import torch
+    _require(qbar, torch.float64, "qbar")
+    _require(kbar, torch.float64, "kbar")
+    b, h, n, D = qbar.shape
+    if tuple(kbar.shape) != (b, h, n, D) or n != grid.n_blk:
+        raise ValueError("qbar/kbar must both be [b, h, n_blk, D] for this grid")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    scores, workspace, row_ptr, col_idx, nnz = _route_outputs(
+        b, h, D, grid, qbar.device, return_scores, workspace, row_ptr, col_idx, nnz)
+    g, s = grid._c(), _shape(b, h, D)
+    _check(_load().bsa_route_pooled(
+        qbar.data_ptr(), kbar.data_ptr(), ctypes.byref(s), ctypes.byref(g), float(top_p),
+        int(k_floor), scale, row_ptr.data_ptr(), col_idx.data_ptr(), nnz.data_ptr(),
+        _ptr(scores), workspace.data_ptr(), workspace.numel(), _stream(qbar)))
     if return_scores:
         return row_ptr, col_idx, nnz, scores
     return row_ptr, col_idx, nnz
@@ -295,10 +351,10 @@ def sparse_attn_fwd(q_t, k_t, v_t, row_ptr, col_idx, grid: Grid,
 def layer(q, k, v, grid: Grid, top_p: float, k_floor: int, scale: Optional[float] = None):
     """Whole path on raster [b, N, h, D] bf16 inputs -> (out [b, N, h, D], row_ptr, col_idx,
     nnz)."""
-    q_t = reorder(q, grid)
-    k_t = reorder(k, grid)
+    q_t, qbar = reorder_pool(q, grid)
+    k_t, kbar = reorder_pool(k, grid)
     v_t = reorder(v, grid)
-    row_ptr, col_idx, nnz = score_and_route(q_t, k_t, grid, top_p, k_floor, scale)
+    row_ptr, col_idx, nnz = route_pooled(qbar, kbar, grid, top_p, k_floor, scale)
     out_t, _ = sparse_attn_fwd(q_t, k_t, v_t, row_ptr, col_idx, grid, scale,
                                return_lse=False)
     return reorder(out_t, grid, inverse=True), row_ptr, col_idx, nnz

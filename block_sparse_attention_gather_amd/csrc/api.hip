@@ -139,6 +139,30 @@ bsa_status bsa_reorder(const void* src, void* dst, const bsa_shape* shape, const
                           (hipStream_t)stream);
 }
 
+bsa_status bsa_reorder_pool(const void* src, void* dst, double* pooled, const bsa_shape* shape,
+                            const bsa_grid* grid, void* stream) {
+    Geometry g;
+    bsa_status st = geometry(grid, &g);
+    if (st != BSA_OK) return st;
+    if ((st = check_shape(shape)) != BSA_OK) return st;
+    if (!src || !dst || !pooled) return fail(BSA_ERR_INVALID_ARG, "src/dst/pooled is NULL");
+    if ((st = check_kernel_dims(shape, g)) != BSA_OK) return st;
+    if (((uintptr_t)src | (uintptr_t)dst) & 15)
+        return fail(BSA_ERR_INVALID_ARG, "src/dst must be 16-byte aligned");
+    if ((uintptr_t)pooled & 7) return fail(BSA_ERR_INVALID_ARG, "pooled must be 8-byte aligned");
+    const int64_t bytes_src = (int64_t)shape->batch * shape->heads * g.N * shape->head_dim * 2;
+    const int64_t bytes_dst = (int64_t)shape->batch * shape->heads * g.Npad * shape->head_dim * 2;
+    const int64_t bytes_pool = (int64_t)shape->batch * shape->heads * g.n_blk * shape->head_dim * 8;
+    const char* s0 = (const char*)src;
+    const char* d0 = (const char*)dst;
+    const char* p0 = (const char*)pooled;
+    if ((s0 < d0 + bytes_dst && d0 < s0 + bytes_src) || (s0 < p0 + bytes_pool && p0 < s0 + bytes_src) ||
+        (d0 < p0 + bytes_pool && p0 < d0 + bytes_dst))
+        return fail(BSA_ERR_INVALID_ARG, "src, dst and pooled must not overlap");
+    return launch_reorder_pool(src, dst, pooled, shape->batch, shape->heads, shape->head_dim, g,
+                               (hipStream_t)stream);
+}
+
 size_t bsa_route_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid) {
     Geometry g;
     if (geometry(grid, &g) != BSA_OK || check_shape(shape) != BSA_OK) return 0;
@@ -167,6 +191,31 @@ bsa_status bsa_score_and_route(const void* q_t, const void* k_t, const bsa_shape
         return fail(BSA_ERR_WORKSPACE, "route workspace: need %zu bytes, 256-byte aligned", need);
     return launch_route(q_t, k_t, shape->batch, shape->heads, shape->head_dim, g, top_p, k_floor,
                         scale, row_ptr, col_idx, nnz, block_scores, ws, (hipStream_t)stream);
+}
+
+bsa_status bsa_route_pooled(const double* qbar, const double* kbar, const bsa_shape* shape,
+                            const bsa_grid* grid, double top_p, int32_t k_floor, double scale,
+                            int32_t* row_ptr, int32_t* col_idx, int32_t* nnz,
+                            double* block_scores, void* ws, size_t ws_bytes, void* stream) {
+    Geometry g;
+    bsa_status st = geometry(grid, &g);
+    if (st != BSA_OK) return st;
+    if ((st = check_shape(shape)) != BSA_OK) return st;
+    if (!qbar || !kbar || !row_ptr || !col_idx || !nnz)
+        return fail(BSA_ERR_INVALID_ARG, "qbar, kbar, row_ptr, col_idx and nnz must be non-NULL");
+    if (!(top_p >= 0.0 && top_p <= 1.0))
+        return fail(BSA_ERR_INVALID_ARG, "top_p must lie in [0, 1] (got %g)", top_p);
+    if (k_floor < 1) return fail(BSA_ERR_INVALID_ARG, "k_floor must be >= 1 (got %d)", k_floor);
+    if (!isfinite(scale)) return fail(BSA_ERR_INVALID_ARG, "scale must be finite");
+    if ((st = check_kernel_dims(shape, g)) != BSA_OK) return st;
+    if ((((uintptr_t)qbar | (uintptr_t)kbar) & 15))
+        return fail(BSA_ERR_INVALID_ARG, "qbar/kbar must be 16-byte aligned");
+    const size_t need = route_ws_bytes(shape->batch, shape->heads, shape->head_dim, g);
+    if (!ws || ws_bytes < need || ((uintptr_t)ws & 255))
+        return fail(BSA_ERR_WORKSPACE, "route workspace: need %zu bytes, 256-byte aligned", need);
+    return launch_route_pooled(qbar, kbar, shape->batch, shape->heads, shape->head_dim, g, top_p,
+                               k_floor, scale, row_ptr, col_idx, nnz, block_scores, ws,
+                               (hipStream_t)stream);
 }
 
 size_t bsa_attn_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid) {

@@ -24,9 +24,11 @@
 // owning 32 query rows.  S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T in
 // registers) leaves each lane one query and 16 keys per 32x32 tile, so the row max is one
 // cross-half exchange and the row sum stays per lane until the end.  P^T is already the B
-// operand layout of O^T = V^T P^T; V is stored transposed in LDS with its keys permuted
-// inside every 16-key group to match, and both LDS tiles have rows padded by 16 bytes so the
-// 32 lanes of a half-wave read distinct banks.
+// operand layout of O^T = V^T P^T.  K and V tiles are copied row-major into LDS by LDS-DMA
+// (global_load_lds); K operands are plain 16-byte reads, V^T operands are transposing reads
+// (ds_read_b64_tr_b16), and the 16-byte chunks of each tile row are XOR-swizzled by the row
+// index (K: c ^ (r mod C), V: c ^ (4r mod C), C = D/8 chunks a row) so neither read pattern
+// has bank conflicts.
 #include "bsa_internal.h"
 
 namespace bsa {
@@ -39,6 +41,7 @@ constexpr int kNQ = 8;             // XCD queues (MI355X: 8 XCDs)
 constexpr int kPlanThreads = 1024;
 constexpr int kMaxHeads = 2048;    // batch * heads supported by the planner
 constexpr int kMaxBlocks = 4096;   // n_blk supported by the planner
+static_assert(kMaxBlocks <= 4096, "the planner packs a row index into 12 bits");
 constexpr int kKcMin = 8;          // smallest chunk (blocks) a row is split into
 constexpr float kRescaleThresh = 8.0f;   // log2 units the running max may lag
 
@@ -82,7 +85,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_global_kernel(
     const int32_t* __restrict__ row_ptr, int32_t n_blk, int32_t nbh, int32_t target,
     int32_t* __restrict__ hdr, int32_t* __restrict__ head_item_off,
     int32_t* __restrict__ head_slot_base) {
-    __shared__ int32_t hitems[kMaxHeads], hslots[kMaxHeads], hrank[kMaxHeads];
+    __shared__ int32_t hitems[kMaxHeads], hslots[kMaxHeads], hcost[kMaxHeads];
     __shared__ int32_t horder[kMaxHeads], hqueue[kMaxHeads];
     __shared__ int64_t qload[kNQ];
     __shared__ int32_t qlen[kNQ], qstart[kNQ], qrun[kNQ];
@@ -91,25 +94,42 @@ __global__ __launch_bounds__(kPlanThreads) void plan_global_kernel(
     const int64_t total = row_ptr[rows];
     int64_t kc64 = (total + target - 1) / target;
     const int32_t Kc = (int32_t)(kc64 < kKcMin ? kKcMin : kc64);
-    for (int h = t; h < nbh; h += kPlanThreads) { hitems[h] = 0; hslots[h] = 0; }
-    __syncthreads();
-    for (int64_t r = t; r < rows; r += kPlanThreads) {
-        const int32_t c = row_ptr[r + 1] - row_ptr[r];
-        int32_t ni = (c + Kc - 1) / Kc;
-        ni = ni < 1 ? 1 : ni;
-        const int h = (int)(r / n_blk);
-        atomicAdd(&hitems[h], ni);
-        if (ni > 1) atomicAdd(&hslots[h], ni);
+    for (int h = t; h < nbh; h += kPlanThreads)
+        hcost[h] = row_ptr[(int64_t)(h + 1) * n_blk] - row_ptr[(int64_t)h * n_blk];
+    // work items and partial slots per head: one wavefront sums one head's rows
+    {
+        const int lane = t & 63, w = t >> 6;
+        for (int h = w; h < nbh; h += kPlanThreads / 64) {
+            int32_t ni_sum = 0, ns_sum = 0;
+#pragma unroll 8
+            for (int i = lane; i < n_blk; i += 64) {
+                const int64_t r = (int64_t)h * n_blk + i;
+                const int32_t c = row_ptr[r + 1] - row_ptr[r];
+                int32_t ni = (c + Kc - 1) / Kc;
+                ni = ni < 1 ? 1 : ni;
+                ni_sum += ni;
+                ns_sum += ni > 1 ? ni : 0;
+            }
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                ni_sum += __shfl_xor(ni_sum, off, 64);
+                ns_sum += __shfl_xor(ns_sum, off, 64);
+            }
+            if (lane == 0) {
+                hitems[h] = ni_sum;
+                hslots[h] = ns_sum;
+            }
+        }
     }
+    __syncthreads();
     // heads ranked by cost (kept blocks) descending, ties by index
     for (int h = t; h < nbh; h += kPlanThreads) {
-        const int32_t ch = row_ptr[(int64_t)(h + 1) * n_blk] - row_ptr[(int64_t)h * n_blk];
+        const int32_t ch = hcost[h];
         int rk = 0;
         for (int h2 = 0; h2 < nbh; ++h2) {
-            const int32_t c2 = row_ptr[(int64_t)(h2 + 1) * n_blk] - row_ptr[(int64_t)h2 * n_blk];
+            const int32_t c2 = hcost[h2];
             rk += (c2 > ch) || (c2 == ch && h2 < h);
         }
-        hrank[h] = rk;
         horder[rk] = h;
     }
     __syncthreads();
@@ -121,7 +141,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_global_kernel(
             int best = 0;
             for (int q = 1; q < kNQ; ++q)
                 if (qload[q] < qload[best]) best = q;
-            qload[best] += row_ptr[(int64_t)(h + 1) * n_blk] - row_ptr[(int64_t)h * n_blk];
+            qload[best] += hcost[h];
             qlen[best] += hitems[h];
             hqueue[h] = best;
         }
@@ -156,15 +176,29 @@ __global__ __launch_bounds__(kPlanThreads) void plan_rows_kernel(
     const int32_t Kc = hdr[kHdrKc];
     for (int i = t; i < n_blk; i += kPlanThreads) cost[i] = row_ptr[base + i + 1] - row_ptr[base + i];
     __syncthreads();
-    for (int i = t; i < n_blk; i += kPlanThreads) {
-        const int32_t ci = cost[i];
-        int rk = 0;
-        for (int i2 = 0; i2 < n_blk; ++i2) {
-            const int32_t c2 = cost[i2];
-            rk += (c2 > ci) || (c2 == ci && i2 < i);
+    // rows by cost descending, ties by row index: bitonic sort of one 32-bit word per row,
+    // (kMaxBlocks - cost) above the 12-bit row index, padding words last
+    int P2 = 2;
+    while (P2 < n_blk) P2 <<= 1;
+    uint32_t* key = (uint32_t*)ord;
+    for (int i = t; i < P2; i += kPlanThreads)
+        key[i] = i < n_blk ? ((uint32_t)(kMaxBlocks - cost[i]) << 12) | (uint32_t)i : 0xffffffffu;
+    __syncthreads();
+    for (int kk = 2; kk <= P2; kk <<= 1)
+        for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+            for (int i = t; i < P2; i += kPlanThreads) {
+                const int l = i ^ jj;
+                if (l > i) {
+                    const uint32_t x = key[i], y = key[l];
+                    if ((x > y) == ((i & kk) == 0)) {
+                        key[i] = y;
+                        key[l] = x;
+                    }
+                }
+            }
+            __syncthreads();
         }
-        ord[rk] = i;
-    }
+    for (int k = t; k < n_blk; k += kPlanThreads) ord[k] = (int32_t)(key[k] & 0xfffu);
     __syncthreads();
     // exclusive scans (in rank order) of items per row and of partial slots per split row
     const int seg = (n_blk + kPlanThreads - 1) / kPlanThreads;

@@ -36,7 +36,15 @@ int attn_max_blocks();
 bsa_status launch_reorder(const void* src, void* dst, int32_t batch, int32_t heads,
                           int32_t D, const Geometry& g, int inverse, hipStream_t s);
 
+bsa_status launch_reorder_pool(const void* src, void* dst, double* pooled, int32_t batch,
+                               int32_t heads, int32_t D, const Geometry& g, hipStream_t s);
+
 size_t route_ws_bytes(int32_t batch, int32_t heads, int32_t D, const Geometry& g);
+bsa_status launch_route_pooled(const double* qbar, const double* kbar, int32_t batch,
+                               int32_t heads, int32_t D, const Geometry& g, double top_p,
+                               int32_t k_floor, double scale, int32_t* row_ptr,
+                               int32_t* col_idx, int32_t* nnz, double* block_scores, void* ws,
+                               hipStream_t s);
 bsa_status launch_route(const void* q_t, const void* k_t, int32_t batch, int32_t heads,
                         int32_t D, const Geometry& g, double top_p, int32_t k_floor,
                         double scale, int32_t* row_ptr, int32_t* col_idx, int32_t* nnz,

@@ -113,6 +113,61 @@ void launch_dir(const uint4* sp, uint4* dp, const GridArgs& ga, dim3 grid, int32
                            sp, dp, ga, heads, dch, N, Npad);
 }
 
+// Forward reorder fused with routing's block pooling: workgroup (j, bh) gathers the B raster
+// rows of block j of (batch, head) bh (head_dim D contiguous elements each), writes them as
+// the contiguous tiled block (pad rows zero) and sums every column over the block's real rows
+// in fp64; pooled[bh][j] = column sums / real rows.  The sums of bf16 values are exact in
+// fp64 for the value ranges involved, so the means equal a separate pooling pass bit for bit.
+template <int D, int B>
+__global__ __launch_bounds__(kReorderThreads) void reorder_pool_kernel(
+    const uint4* __restrict__ src, uint4* __restrict__ dst, double* __restrict__ pooled,
+    GridArgs g, int32_t heads, uint32_t N, uint32_t Npad) {
+    constexpr int DCH = D / 8;                    // 16-byte chunks per row
+    constexpr int RPP = kReorderThreads / DCH;    // rows per pass
+    constexpr int NP = B / RPP;                   // passes (rows per thread)
+    __shared__ double red[RPP][D + 1];
+    const int t = threadIdx.x;
+    const int dc = t % DCH, rp = t / DCH;
+    const uint32_t j = blockIdx.x;
+    const uint32_t bh = blockIdx.y;
+    const uint32_t b = bh / (uint32_t)heads, h = bh - b * (uint32_t)heads;
+    const uint32_t lo = j * B;
+    const uint32_t hi = min(lo + (uint32_t)B, N);
+    uint4 v[NP];
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+        const uint32_t p = lo + rp + RPP * k;
+        if (p < N) {
+            const uint32_t n = tile_pos_to_raster(p, g);
+            v[k] = src[(((size_t)b * N + n) * heads + h) * DCH + dc];
+        } else {
+            v[k] = make_uint4(0, 0, 0, 0);
+        }
+    }
+    double acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+        const uint32_t p = lo + rp + RPP * k;
+        dst[((size_t)bh * Npad + p) * DCH + dc] = v[k];
+        const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            acc[2 * u] += (double)__uint_as_float(w[u] << 16);
+            acc[2 * u + 1] += (double)__uint_as_float(w[u] & 0xffff0000u);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[rp][dc * 8 + e] = acc[e];
+    __syncthreads();
+    for (int d = t; d < D; d += kReorderThreads) {
+        double sum = 0.0;
+        for (int r = 0; r < RPP; ++r) sum += red[r][d];
+        pooled[((size_t)bh * gridDim.x + j) * D + d] = sum / (double)(hi - lo);
+    }
+}
+
 }  // namespace
 
 bsa_status launch_reorder(const void* src, void* dst, int32_t batch, int32_t heads, int32_t D,
@@ -134,6 +189,29 @@ bsa_status launch_reorder(const void* src, void* dst, int32_t batch, int32_t hea
     else
         launch_dir<0>(sp, dp, ga, grid, heads, D / 8, N, Npad, inverse, s);
     return check_launch("reorder");
+}
+
+bsa_status launch_reorder_pool(const void* src, void* dst, double* pooled, int32_t batch,
+                               int32_t heads, int32_t D, const Geometry& g, hipStream_t s) {
+    GridArgs ga{g.T, g.H, g.W, g.tt, g.th, g.tw};
+    const dim3 grid((unsigned)g.n_blk, (unsigned)(batch * heads));
+    const uint4* sp = (const uint4*)src;
+    uint4* dp = (uint4*)dst;
+    const uint32_t N = (uint32_t)g.N, Npad = (uint32_t)g.Npad;
+    const dim3 blk(kReorderThreads);
+    if (D == 128 && g.B == 128)
+        hipLaunchKernelGGL((reorder_pool_kernel<128, 128>), grid, blk, 0, s, sp, dp, pooled, ga,
+                           heads, N, Npad);
+    else if (D == 128)
+        hipLaunchKernelGGL((reorder_pool_kernel<128, 64>), grid, blk, 0, s, sp, dp, pooled, ga,
+                           heads, N, Npad);
+    else if (g.B == 128)
+        hipLaunchKernelGGL((reorder_pool_kernel<64, 128>), grid, blk, 0, s, sp, dp, pooled, ga,
+                           heads, N, Npad);
+    else
+        hipLaunchKernelGGL((reorder_pool_kernel<64, 64>), grid, blk, 0, s, sp, dp, pooled, ga,
+                           heads, N, Npad);
+    return check_launch("reorder_pool");
 }
 
 }  // namespace bsa

@@ -501,38 +501,61 @@ __global__ __launch_bounds__(kSortRows * 64) void route_sort_kernel(SortArgs a) 
 // scan: one workgroup; counts -> row_ptr (exclusive, rows + 1 entries) and nnz
 // ---------------------------------------------------------------------------------------
 constexpr int kScanThreads = 1024;
+constexpr int kScanTile = 4 * kScanThreads;    // counts per pass, four per thread
 
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ row_ptr,
                                                             int32_t* __restrict__ nnz,
                                                             int64_t rows) {
-    __shared__ int64_t part[kScanThreads];
+    __shared__ int32_t wtot[kScanThreads / 64];
     const int t = threadIdx.x;
-    const int64_t seg = (rows + kScanThreads - 1) / kScanThreads;
-    const int64_t lo = min(rows, t * seg), hi = min(rows, lo + seg);
-    int64_t local = 0;
-    for (int64_t r = lo; r < hi; ++r) local += counts[r];
-    part[t] = local;
-    __syncthreads();
-    for (int off = 1; off < kScanThreads; off <<= 1) {
-        const int64_t add = t >= off ? part[t - off] : 0;
+    const int lane = t & 63, w = t >> 6;
+    int32_t carry = 0;                     // total of the earlier passes (nnz fits int32)
+    for (int64_t base = 0; base < rows; base += kScanTile) {
+        const int64_t i0 = base + 4 * t;
+        int32_t v[4];
+        if (i0 + 3 < rows) {
+            const int4 x = *(const int4*)(counts + i0);      // counts is 256-byte aligned
+            v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = i0 + u < rows ? counts[i0 + u] : 0;
+        }
+        const int32_t tsum = v[0] + v[1] + v[2] + v[3];
+        int32_t incl = tsum;                                 // inclusive over the wavefront
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int32_t u = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += u;
+        }
+        if (lane == 63) wtot[w] = incl;
         __syncthreads();
-        part[t] += add;
-        __syncthreads();
+        int32_t before = carry, total = carry;
+#pragma unroll
+        for (int k = 0; k < kScanThreads / 64; ++k) {
+            const int32_t x = wtot[k];
+            before += k < w ? x : 0;
+            total += x;
+        }
+        __syncthreads();                                     // wtot is rewritten next pass
+        int32_t run = before + incl - tsum;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (i0 + u < rows) row_ptr[i0 + u] = run;
+            run += v[u];
+        }
+        carry = total;
     }
-    int64_t run = part[t] - local;
-    for (int64_t r = lo; r < hi; ++r) {
-        row_ptr[r] = (int32_t)run;
-        run += counts[r];
-    }
-    if (t == kScanThreads - 1) {
-        row_ptr[rows] = (int32_t)part[t];
-        nnz[0] = (int32_t)part[t];
+    if (t == 0) {
+        row_ptr[rows] = carry;
+        nnz[0] = carry;
     }
 }
 
 // ---------------------------------------------------------------------------------------
-// fill: one wavefront per row; grid (ceil(rows / 4)), 256 threads
+// fill: one wavefront per row; grid (ceil(rows / 4)), 256 threads.  Each half-wavefront expands
+// one 32-bit bitmap word per pass, lane b writing column 32 w + b at its rank among the set
+// bits, so a pass stores two contiguous runs of ascending columns.
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void fill_kernel(const uint32_t* __restrict__ bitmap,
                                                         const int32_t* __restrict__ row_ptr,
@@ -542,24 +565,16 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(const uint32_t* __restri
     const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
     if (row >= rows) return;
     const uint32_t* bm = bitmap + row * nwords;
+    const int bit = lane & 31, hi = lane >> 5;
     int32_t base = row_ptr[row];
-    for (int w0 = 0; w0 < nwords; w0 += 64) {
-        const int w = w0 + lane;
+    for (int w0 = 0; w0 < nwords; w0 += 2) {
+        const int w = w0 + hi;
         const uint32_t word = w < nwords ? bm[w] : 0u;
-        const int cnt = __popc(word);
-        int incl = cnt;
-        for (int off = 1; off < 64; off <<= 1) {
-            const int up = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += up;
-        }
-        int pos = base + incl - cnt;
-        uint32_t m = word;
-        while (m) {
-            const int bit = __ffs(m) - 1;
-            col_idx[pos++] = w * 32 + bit;
-            m &= m - 1;
-        }
-        base += __shfl(incl, 63, 64);
+        const int c0 = __popc(__shfl(word, 0, 64));         // set bits of word w0
+        const int c1 = __popc(__shfl(word, 32, 64));        // and of word w0 + 1
+        if ((word >> bit) & 1u)
+            col_idx[base + (hi ? c0 : 0) + __popc(word & ((1u << bit) - 1u))] = w * 32 + bit;
+        base += c0 + c1;
     }
 }
 
@@ -597,11 +612,7 @@ bsa_status launch_route(const void* q_t, const void* k_t, int32_t batch, int32_t
     unsigned char* w = (unsigned char*)ws;
     double* qbar = (double*)(w + L.qbar);
     double* kbar = (double*)(w + L.kbar);
-    uint32_t* bitmap = (uint32_t*)(w + L.bitmap);
-    int32_t* counts = (int32_t*)(w + L.counts);
     const int32_t bh = batch * heads;
-    const int64_t rows = (int64_t)bh * g.n_blk;
-
     dim3 pgrid(g.n_blk, bh, 2);
     if (D == 64)
         hipLaunchKernelGGL(pool_kernel<64>, pgrid, dim3(kThreads), 0, s, (const uint4*)q_t,
@@ -611,6 +622,22 @@ bsa_status launch_route(const void* q_t, const void* k_t, int32_t batch, int32_t
                            (const uint4*)k_t, qbar, kbar, g.N, g.Npad, g.B, g.n_blk);
     bsa_status st = check_launch("pool");
     if (st != BSA_OK) return st;
+    return launch_route_pooled(qbar, kbar, batch, heads, D, g, top_p, k_floor, scale, row_ptr,
+                               col_idx, nnz, block_scores, ws, s);
+}
+
+bsa_status launch_route_pooled(const double* qbar, const double* kbar, int32_t batch,
+                               int32_t heads, int32_t D, const Geometry& g, double top_p,
+                               int32_t k_floor, double scale, int32_t* row_ptr,
+                               int32_t* col_idx, int32_t* nnz, double* block_scores, void* ws,
+                               hipStream_t s) {
+    const RouteLayout L = route_layout(batch, heads, D, g);
+    unsigned char* w = (unsigned char*)ws;
+    uint32_t* bitmap = (uint32_t*)(w + L.bitmap);
+    int32_t* counts = (int32_t*)(w + L.counts);
+    const int32_t bh = batch * heads;
+    const int64_t rows = (int64_t)bh * g.n_blk;
+    bsa_status st;
 
     RouteArgs a;
     a.qbar = qbar;

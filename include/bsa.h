@@ -12,6 +12,10 @@
  *   bsa_score_and_route  per-block mean pooling, pooled block scores, Top-p/Top-k -> CSR
  *   bsa_sparse_attn_fwd  exact block-sparse attention over the CSR lists
  *
+ * Two more calls split the same work differently: bsa_reorder_pool does the forward
+ * permutation of Q (or K) and its block means in one pass, and bsa_route_pooled routes from
+ * those means, so Q and K are read once instead of twice.
+ *
  * Conventions shared by every call
  *   - Tensor arguments are DEVICE pointers (HIP device memory of the current device).  The
  *     caller allocates and owns every buffer, workspaces included; the library never
@@ -83,6 +87,17 @@ BSA_API int32_t bsa_padded_len(const bsa_grid* grid);
 BSA_API bsa_status bsa_reorder(const void* src, void* dst, const bsa_shape* shape,
                        const bsa_grid* grid, int32_t inverse, void* stream);
 
+/* Forward reorder fused with the block pooling of routing (FVAttn abstract: video-aware
+ * blocks, pooled into one mean per block for the router):
+ *   dst    as bsa_reorder(inverse = 0): tiled bf16 [batch, heads, Npad, D], pad rows zero;
+ *   pooled fp64 [batch, heads, n_blk, D]: pooled[b][h][j] = mean of dst rows j*block ..
+ *          min((j+1)*block, N) - 1 (the block's real tokens), bit-identical to the pooling
+ *          inside bsa_score_and_route.
+ * head_dim 64 or 128, block 64 or 128.  src and dst 16-byte aligned, pooled 8-byte aligned;
+ * no two of the three may overlap (BSA_ERR_INVALID_ARG). */
+BSA_API bsa_status bsa_reorder_pool(const void* src, void* dst, double* pooled,
+                                    const bsa_shape* shape, const bsa_grid* grid, void* stream);
+
 /* ---- 2. routing frontend: pooled block scores, Top-p with a Top-k floor (FVAttn) ---- */
 /* Workspace bytes bsa_score_and_route needs (depends on shape and grid only). */
 BSA_API size_t bsa_route_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid);
@@ -93,6 +108,10 @@ BSA_API size_t bsa_route_workspace_bytes(const bsa_shape* shape, const bsa_grid*
  *   order j by s_ij descending (equal scores: smaller j first), keep the shortest prefix
  *   whose cumulative mass reaches top_p (top_p >= 1: all; top_p == 0: none; all if rounding
  *   never reaches top_p), then raise the count to min(n_blk, k_floor).
+ *   Rows of up to 2048 blocks rank by the score's order-preserving 64-bit image with its low
+ *   log2(P) bits (P = max(64, next power of two >= n_blk), at most 11 bits) dropped, so two
+ *   scores within 2^-41 of each other (relative) may rank by index instead; the masses and
+ *   the prefix use the exact scores.  Longer rows rank by the exact scores.
  * Outputs, CSR over rows:
  *   row_ptr [rows + 1] int32, row_ptr[0] = 0;
  *   col_idx capacity rows*n_blk int32 (worst case), kept key blocks of each row ascending;
@@ -107,6 +126,16 @@ BSA_API bsa_status bsa_score_and_route(const void* q_t, const void* k_t, const b
                                double scale, int32_t* row_ptr, int32_t* col_idx,
                                int32_t* nnz, double* block_scores, void* ws,
                                size_t ws_bytes, void* stream);
+
+/* bsa_score_and_route without its pooling step: qbar and kbar are the block means
+ * [batch, heads, n_blk, D] fp64 (as bsa_reorder_pool writes them, 16-byte aligned); every
+ * other argument, output, error and the workspace (bsa_route_workspace_bytes) are those of
+ * bsa_score_and_route, and for the same Q and K the outputs are identical. */
+BSA_API bsa_status bsa_route_pooled(const double* qbar, const double* kbar,
+                                    const bsa_shape* shape, const bsa_grid* grid, double top_p,
+                                    int32_t k_floor, double scale, int32_t* row_ptr,
+                                    int32_t* col_idx, int32_t* nnz, double* block_scores,
+                                    void* ws, size_t ws_bytes, void* stream);
 
 /* ---- 3. exact block-sparse attention (online softmax over the kept blocks) --------- */
 /* Workspace bytes bsa_sparse_attn_fwd needs: worst case over every possible CSR, so the host

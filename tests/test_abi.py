@@ -31,7 +31,7 @@ def test_header_compiles_as_c99_and_cxx(tmp_path):
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     lib = ctypes.CDLL(bsa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -121,6 +121,45 @@ def test_reorder_validation():
     assert L.bsa_reorder(FAKE, FAKE + 64, ctypes.byref(s), ctypes.byref(g), 0, None) == -1
     assert "overlap" in L.bsa_last_error().decode()
     assert L.bsa_reorder(FAKE, FAKE, None, ctypes.byref(g), 0, None) == -1
+
+
+def test_reorder_pool_validation():
+    L = bsa.lib()
+    g = bsa.Grid(2, 16, 16, (4, 4, 4), 64)._c()
+    s = bsa._Shape(1, 2, 64)
+    far = FAKE + (1 << 28)
+    assert L.bsa_reorder_pool(FAKE, FAKE + (1 << 24), None, ctypes.byref(s), ctypes.byref(g),
+                              None) == -1
+    assert "NULL" in L.bsa_last_error().decode()
+    s96 = bsa._Shape(1, 2, 96)                       # the pooled path is built for 64 and 128
+    assert L.bsa_reorder_pool(FAKE, FAKE + (1 << 24), far, ctypes.byref(s96), ctypes.byref(g),
+                              None) == -2
+    assert L.bsa_reorder_pool(FAKE, FAKE + (1 << 24), FAKE + 4, ctypes.byref(s),
+                              ctypes.byref(g), None) == -1        # pooled overlaps src
+    assert L.bsa_reorder_pool(FAKE, FAKE + (1 << 24), far + 4, ctypes.byref(s), ctypes.byref(g),
+                              None) == -1                         # pooled misaligned
+    assert "aligned" in L.bsa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(q=None), -1, "non-NULL"),
+    (dict(top_p=1.5), -1, "top_p"),
+    (dict(k_floor=0), -1, "k_floor"),
+    (dict(shape=(1, 2, 96)), -2, "head_dim"),
+    (dict(ws_bytes=16), -3, "workspace"),
+    (dict(q=FAKE + 8), -1, "aligned"),
+])
+def test_route_pooled_validation(kw, status, msg):
+    L = bsa.lib()
+    g = bsa.Grid(2, 16, 16, (4, 4, 4), 64)._c()
+    s = bsa._Shape(*kw.pop("shape", (1, 2, 64)))
+    a = dict(q=FAKE, k=FAKE, top_p=0.9, k_floor=2, ws_bytes=1 << 30)
+    a.update(kw)
+    st = L.bsa_route_pooled(a["q"], a["k"], ctypes.byref(s), ctypes.byref(g), a["top_p"],
+                            a["k_floor"], 0.125, FAKE, FAKE, FAKE, None, FAKE, a["ws_bytes"],
+                            None)
+    assert st == status, (st, L.bsa_last_error())
+    assert msg in L.bsa_last_error().decode()
 
 
 def test_attn_validation_before_device_query():
