@@ -92,6 +92,8 @@ def _load():
         "bsa_route_workspace_bytes": (SZ, [S, G]),
         "bsa_score_and_route": (I32, [P, P, S, G, F64, I32, F64, P, P, P, P, P, SZ, P]),
         "bsa_route_pooled": (I32, [P, P, S, G, F64, I32, F64, P, P, P, P, P, SZ, P]),
+        "bsa_stripe_workspace_bytes": (SZ, [S, G]),
+        "bsa_stripe_mask": (I32, [P, S, G, P, P, P, P, SZ, P]),
         "bsa_attn_workspace_bytes": (SZ, [S, G]),
         "bsa_sparse_attn_fwd": (I32, [P, P, P, P, P, S, G, F32, P, P, P, SZ, P]),
         "bsa_last_error": (ctypes.c_char_p, []),
@@ -309,6 +311,41 @@ def route_pooled(qbar, kbar, grid: Grid, top_p: float, k_floor: int,
         _ptr(scores), workspace.data_ptr(), workspace.numel(), _stream(qbar)))
     if return_scores:
         return row_ptr, col_idx, nnz, scores
+    return row_ptr, col_idx, nnz
+
+
+def stripe_mask(params, batch: int, heads: int, D: int, grid: Grid, device="cuda:0",
+                workspace=None, row_ptr=None, col_idx=None, nnz=None):
+    """Static periodic-stripe masks -> CSR (row_ptr, col_idx, nnz) in the routing's format.
+
+    params: one (Tw, To, Ts, Sw, So, Ss) for every head, or a list of `heads` of them."""
+    import torch
+    p = list(params)
+    if p and not isinstance(p[0], (tuple, list)):
+        p = [tuple(p)] * heads
+    if len(p) != heads or any(len(x) != 6 for x in p):
+        raise ValueError("params: one (Tw, To, Ts, Sw, So, Ss) per head")
+    arr = (ctypes.c_int32 * (6 * heads))(*[int(v) for x in p for v in x])
+    dev = torch.device(device)
+    rows = batch * heads * grid.n_blk
+    if row_ptr is None:
+        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(rows * grid.n_blk, dtype=torch.int32, device=dev)
+    if nnz is None:
+        nnz = torch.empty(1, dtype=torch.int32, device=dev)
+    for t, n, size in ((row_ptr, "row_ptr", rows + 1), (col_idx, "col_idx", rows * grid.n_blk),
+                       (nnz, "nnz", 1)):
+        _require(t, torch.int32, n)
+        if t.numel() < size:
+            raise ValueError(f"{n} needs {size} int32 entries")
+    g, s = grid._c(), _shape(batch, heads, D)
+    if workspace is None:
+        need = int(_load().bsa_stripe_workspace_bytes(ctypes.byref(s), ctypes.byref(g)))
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(_load().bsa_stripe_mask(arr, ctypes.byref(s), ctypes.byref(g), row_ptr.data_ptr(),
+                                   col_idx.data_ptr(), nnz.data_ptr(), workspace.data_ptr(),
+                                   workspace.numel(), _stream(row_ptr)))
     return row_ptr, col_idx, nnz
 
 

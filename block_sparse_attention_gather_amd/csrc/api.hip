@@ -218,6 +218,35 @@ bsa_status bsa_route_pooled(const double* qbar, const double* kbar, const bsa_sh
                                (hipStream_t)stream);
 }
 
+size_t bsa_stripe_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid) {
+    Geometry g;
+    if (geometry(grid, &g) != BSA_OK || check_shape(shape) != BSA_OK) return 0;
+    return stripe_ws_bytes(shape->batch, shape->heads, g);
+}
+
+bsa_status bsa_stripe_mask(const bsa_stripe* params, const bsa_shape* shape,
+                           const bsa_grid* grid, int32_t* row_ptr, int32_t* col_idx,
+                           int32_t* nnz, void* ws, size_t ws_bytes, void* stream) {
+    Geometry g;
+    bsa_status st = geometry(grid, &g);
+    if (st != BSA_OK) return st;
+    if ((st = check_shape(shape)) != BSA_OK) return st;
+    if (!params || !row_ptr || !col_idx || !nnz)
+        return fail(BSA_ERR_INVALID_ARG, "params, row_ptr, col_idx and nnz must be non-NULL");
+    for (int32_t h = 0; h < shape->heads; ++h) {
+        const bsa_stripe& m = params[h];
+        if (!(m.Tw >= 1 && m.Tw <= m.Ts && m.Sw >= 1 && m.Sw <= m.Ss))
+            return fail(BSA_ERR_INVALID_ARG,
+                        "stripe parameters of head %d need 1 <= Tw <= Ts and 1 <= Sw <= Ss", h);
+    }
+    if ((st = check_kernel_dims(shape, g)) != BSA_OK) return st;
+    const size_t need = stripe_ws_bytes(shape->batch, shape->heads, g);
+    if (!ws || ws_bytes < need || ((uintptr_t)ws & 255))
+        return fail(BSA_ERR_WORKSPACE, "stripe workspace: need %zu bytes, 256-byte aligned", need);
+    return launch_stripe((const int32_t*)params, shape->batch, shape->heads, g, row_ptr, col_idx,
+                         nnz, ws, (hipStream_t)stream);
+}
+
 size_t bsa_attn_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid) {
     Geometry g;
     if (geometry(grid, &g) != BSA_OK || check_shape(shape) != BSA_OK) return 0;

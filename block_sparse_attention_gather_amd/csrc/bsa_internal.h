@@ -17,6 +17,37 @@ struct Geometry {
     int64_t Npad;     // n_blk * B
 };
 
+// 3D-tile grid as kernel arguments, and the tile-order position -> raster token map that
+// the reorder and the stripe-mask kernels share.
+struct GridArgs {
+    int32_t T, H, W, tt, th, tw;
+};
+
+// Tile-order position p -> raster token n, in 32-bit arithmetic (N < 2^31 is checked on the
+// host, so every intermediate fits).
+static __device__ __forceinline__ uint32_t tile_pos_to_raster(uint32_t p, const GridArgs& g) {
+    const uint32_t T = g.T, H = g.H, W = g.W, tt = g.tt, th = g.th, tw = g.tw;
+    const uint32_t slab = tt * H * W;
+    const uint32_t it = p / slab;
+    uint32_t r = p - it * slab;
+    const uint32_t et = min(tt, T - it * tt);
+    const uint32_t row = et * th * W;
+    const uint32_t ih = r / row;
+    r -= ih * row;
+    const uint32_t eh = min(th, H - ih * th);
+    const uint32_t tile = et * eh * tw;
+    const uint32_t iw = r / tile;
+    r -= iw * tile;
+    const uint32_t ew = min(tw, W - iw * tw);
+    const uint32_t plane = eh * ew;
+    const uint32_t rt = r / plane;
+    r -= rt * plane;
+    const uint32_t rh = r / ew;
+    const uint32_t rw = r - rh * ew;
+    const uint32_t t = it * tt + rt, h = ih * th + rh, w = iw * tw + rw;
+    return (t * H + h) * W + w;
+}
+
 // ---- error reporting (thread-local message, see bsa_last_error) ---------------------
 bsa_status fail(bsa_status st, const char* fmt, ...);
 bsa_status check_launch(const char* what);
@@ -49,6 +80,11 @@ bsa_status launch_route(const void* q_t, const void* k_t, int32_t batch, int32_t
                         int32_t D, const Geometry& g, double top_p, int32_t k_floor,
                         double scale, int32_t* row_ptr, int32_t* col_idx, int32_t* nnz,
                         double* block_scores, void* ws, hipStream_t s);
+
+size_t stripe_ws_bytes(int32_t batch, int32_t heads, const Geometry& g);
+bsa_status launch_stripe(const int32_t* params_host, int32_t batch, int32_t heads,
+                         const Geometry& g, int32_t* row_ptr, int32_t* col_idx, int32_t* nnz,
+                         void* ws, hipStream_t s);
 
 size_t attn_ws_bytes(int32_t batch, int32_t heads, int32_t D, const Geometry& g, int slots);
 bsa_status launch_attn(const void* q_t, const void* k_t, const void* v_t,

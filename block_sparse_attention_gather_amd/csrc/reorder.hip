@@ -15,35 +15,6 @@
 namespace bsa {
 namespace {
 
-struct GridArgs {
-    int32_t T, H, W, tt, th, tw;
-};
-
-// Tile-order position p -> raster token n, in 32-bit arithmetic (N < 2^31 is checked on the
-// host, so every intermediate fits).
-__device__ __forceinline__ uint32_t tile_pos_to_raster(uint32_t p, const GridArgs& g) {
-    const uint32_t T = g.T, H = g.H, W = g.W, tt = g.tt, th = g.th, tw = g.tw;
-    const uint32_t slab = tt * H * W;
-    const uint32_t it = p / slab;
-    uint32_t r = p - it * slab;
-    const uint32_t et = min(tt, T - it * tt);
-    const uint32_t row = et * th * W;
-    const uint32_t ih = r / row;
-    r -= ih * row;
-    const uint32_t eh = min(th, H - ih * th);
-    const uint32_t tile = et * eh * tw;
-    const uint32_t iw = r / tile;
-    r -= iw * tile;
-    const uint32_t ew = min(tw, W - iw * tw);
-    const uint32_t plane = eh * ew;
-    const uint32_t rt = r / plane;
-    r -= rt * plane;
-    const uint32_t rh = r / ew;
-    const uint32_t rw = r - rh * ew;
-    const uint32_t t = it * tt + rt, h = ih * th + rh, w = iw * tw + rw;
-    return (t * H + h) * W + w;
-}
-
 constexpr int kReorderThreads = 256;
 
 // One wavefront per tile position p of batch blockIdx.y moves one token: the heads * D

@@ -578,6 +578,78 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(const uint32_t* __restri
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Static periodic-stripe masks (PSA page, "Approach": one six-parameter mask
+// M(Tw, To, Ts, Sw, So, Ss) per head, run by the same block-sparse kernel).  Block coordinates
+// are those of the tile holding the block's first token: bt = t / tt, bs = (h / th) nW + w / tw.
+// Key block j is kept for query block i iff (bt_j - bt_i - To) mod Ts < Tw and
+// (bs_j - bs_i - So) mod Ss < Sw (non-negative remainders).  One wavefront per row, four rows
+// per workgroup; 64 key blocks per ballot give two bitmap words.  The coordinates of every
+// block are computed once per call (`coord_kernel`) into the workspace.
+// ---------------------------------------------------------------------------------------
+struct StripeArgs {
+    const int32_t* params;  // [heads][6] = Tw, To, Ts, Sw, So, Ss
+    int2* coords;           // [n_blk] (bt, bs)
+    uint32_t* bitmap;       // [rows][nwords]
+    int32_t* counts;        // [rows]
+    GridArgs g;
+    int32_t B, n_blk, heads, nwords;
+    int64_t rows;
+};
+
+__device__ __forceinline__ void block_coord(int32_t j, const StripeArgs& a, int32_t& bt,
+                                            int32_t& bs) {
+    const uint32_t n = tile_pos_to_raster((uint32_t)j * (uint32_t)a.B, a.g);
+    const uint32_t HW = (uint32_t)a.g.H * (uint32_t)a.g.W;
+    const uint32_t t = n / HW;
+    const uint32_t r = n - t * HW;
+    const uint32_t h = r / (uint32_t)a.g.W;
+    const uint32_t w = r - h * (uint32_t)a.g.W;
+    const int32_t nW = (a.g.W + a.g.tw - 1) / a.g.tw;
+    bt = (int32_t)(t / (uint32_t)a.g.tt);
+    bs = (int32_t)(h / (uint32_t)a.g.th) * nW + (int32_t)(w / (uint32_t)a.g.tw);
+}
+
+__global__ __launch_bounds__(kThreads) void coord_kernel(StripeArgs a) {
+    const int32_t j = blockIdx.x * kThreads + threadIdx.x;
+    if (j >= a.n_blk) return;
+    int32_t bt, bs;
+    block_coord(j, a, bt, bs);
+    a.coords[j] = make_int2(bt, bs);
+}
+
+__device__ __forceinline__ int32_t nonneg_mod(int32_t x, int32_t m) {
+    const int32_t r = x % m;
+    return r < 0 ? r + m : r;
+}
+
+__global__ __launch_bounds__(kThreads) void stripe_kernel(StripeArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (row >= a.rows) return;
+    const int32_t n = a.n_blk;
+    const int64_t bh = row / n;
+    const int32_t i = (int32_t)(row - bh * n);
+    const int32_t* p = a.params + 6 * (int32_t)(bh % a.heads);
+    const int32_t Tw = p[0], To = p[1], Ts = p[2], Sw = p[3], So = p[4], Ss = p[5];
+    const int2 ci = a.coords[i];
+    int32_t count = 0;
+    for (int32_t j0 = 0; j0 < n; j0 += 64) {
+        const int32_t j = j0 + lane;
+        bool keep = false;
+        if (j < n) {
+            const int2 cj = a.coords[j];
+            keep = nonneg_mod(cj.x - ci.x - To, Ts) < Tw && nonneg_mod(cj.y - ci.y - So, Ss) < Sw;
+        }
+        const uint64_t m = __ballot(keep);
+        count += __popcll(m);
+        const int32_t w0 = j0 >> 5;
+        if (lane == 0) a.bitmap[row * a.nwords + w0] = (uint32_t)m;
+        if (lane == 1 && w0 + 1 < a.nwords) a.bitmap[row * a.nwords + w0 + 1] = (uint32_t)(m >> 32);
+    }
+    if (lane == 0) a.counts[row] = count;
+}
+
 struct RouteLayout {
     size_t qbar, kbar, bitmap, counts, scores, total;
 };
@@ -714,6 +786,51 @@ bsa_status launch_route_pooled(const double* qbar, const double* kbar, int32_t b
 
     hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, s,
                        bitmap, row_ptr, col_idx, rows, a.nwords);
+    return check_launch("fill");
+}
+
+size_t stripe_ws_bytes(int32_t batch, int32_t heads, const Geometry& g) {
+    const size_t rows = (size_t)batch * heads * g.n_blk;
+    const size_t nwords = (g.n_blk + 31) / 32;
+    return align_up(rows * nwords * 4, 256) + align_up(rows * 4, 256) +
+           align_up((size_t)heads * 6 * 4, 256) + align_up((size_t)g.n_blk * 8, 256);
+}
+
+bsa_status launch_stripe(const int32_t* params_host, int32_t batch, int32_t heads,
+                         const Geometry& g, int32_t* row_ptr, int32_t* col_idx, int32_t* nnz,
+                         void* ws, hipStream_t s) {
+    const int64_t rows = (int64_t)batch * heads * g.n_blk;
+    const int32_t nwords = (g.n_blk + 31) / 32;
+    unsigned char* w = (unsigned char*)ws;
+    StripeArgs a;
+    a.bitmap = (uint32_t*)w;
+    a.counts = (int32_t*)(w + align_up((size_t)rows * nwords * 4, 256));
+    int32_t* params = (int32_t*)(w + align_up((size_t)rows * nwords * 4, 256) +
+                                 align_up((size_t)rows * 4, 256));
+    a.coords = (int2*)((unsigned char*)params + align_up((size_t)heads * 6 * 4, 256));
+    if (hipMemcpyAsync(params, params_host, (size_t)heads * 6 * 4, hipMemcpyHostToDevice, s) !=
+        hipSuccess)
+        return fail(BSA_ERR_HIP, "stripe parameters: copy to the workspace failed");
+    a.params = params;
+    a.g = GridArgs{g.T, g.H, g.W, g.tt, g.th, g.tw};
+    a.B = g.B;
+    a.n_blk = g.n_blk;
+    a.heads = heads;
+    a.nwords = nwords;
+    a.rows = rows;
+    hipLaunchKernelGGL(coord_kernel, dim3((unsigned)((g.n_blk + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, s, a);
+    bsa_status st = check_launch("stripe coordinates");
+    if (st != BSA_OK) return st;
+    hipLaunchKernelGGL(stripe_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, s, a);
+    st = check_launch("stripe");
+    if (st != BSA_OK) return st;
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a.counts, row_ptr, nnz,
+                       rows);
+    st = check_launch("scan");
+    if (st != BSA_OK) return st;
+    hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, s,
+                       a.bitmap, row_ptr, col_idx, rows, nwords);
     return check_launch("fill");
 }
 

@@ -14,7 +14,9 @@
  *
  * Two more calls split the same work differently: bsa_reorder_pool does the forward
  * permutation of Q (or K) and its block means in one pass, and bsa_route_pooled routes from
- * those means, so Q and K are read once instead of twice.
+ * those means, so Q and K are read once instead of twice.  bsa_stripe_mask emits static
+ * periodic-stripe masks (PSA page) in the same CSR format, as a second workload for
+ * bsa_sparse_attn_fwd.
  *
  * Conventions shared by every call
  *   - Tensor arguments are DEVICE pointers (HIP device memory of the current device).  The
@@ -136,6 +138,34 @@ BSA_API bsa_status bsa_route_pooled(const double* qbar, const double* kbar,
                                     int32_t k_floor, double scale, int32_t* row_ptr,
                                     int32_t* col_idx, int32_t* nnz, double* block_scores,
                                     void* ws, size_t ws_bytes, void* stream);
+
+/* ---- 2b. static periodic-stripe masks (PSA page, "Approach") ----------------------- */
+/* One six-parameter mask M(Tw, To, Ts, Sw, So, Ss) per head.  The page names the parameters
+ * without defining them; reading used here (T = temporal, S = spatial; w = stripe width,
+ * o = offset, s = period): a block's coordinates are those of the 3D tile holding its first
+ * token, bt = t / tile_t and bs = (h / tile_h) * nW + w / tile_w with nW = ceil(W / tile_w);
+ * query block i keeps key block j iff
+ *     (bt_j - bt_i - To) mod Ts < Tw   and   (bs_j - bs_i - So) mod Ss < Sw
+ * (non-negative remainders).  Requires 1 <= Tw <= Ts and 1 <= Sw <= Ss. */
+typedef struct {
+    int32_t Tw, To, Ts, Sw, So, Ss;
+} bsa_stripe;
+
+/* Workspace bytes bsa_stripe_mask needs (depends on shape and grid only). */
+BSA_API size_t bsa_stripe_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid);
+
+/* The stripe masks of every (batch, head) as CSR, in the format bsa_score_and_route writes
+ * (rows r = (b*heads + h)*n_blk + i, columns ascending, nnz = row_ptr[rows] on the device),
+ * ready for bsa_sparse_attn_fwd.
+ * params: HOST array of `heads` parameter sets (head h uses params[h] for every batch); it is
+ *         validated on the host, then copied into the workspace on `stream`, so the caller may
+ *         reuse it when the call returns.
+ * Errors: NULL pointers or a parameter set outside the ranges above -> BSA_ERR_INVALID_ARG;
+ * head_dim/block/size limits as bsa_score_and_route; ws smaller than
+ * bsa_stripe_workspace_bytes() or not 256-byte aligned -> BSA_ERR_WORKSPACE. */
+BSA_API bsa_status bsa_stripe_mask(const bsa_stripe* params, const bsa_shape* shape,
+                                   const bsa_grid* grid, int32_t* row_ptr, int32_t* col_idx,
+                                   int32_t* nnz, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- 3. exact block-sparse attention (online softmax over the kept blocks) --------- */
 /* Workspace bytes bsa_sparse_attn_fwd needs: worst case over every possible CSR, so the host

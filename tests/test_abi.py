@@ -31,7 +31,7 @@ def test_header_compiles_as_c99_and_cxx(tmp_path):
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     lib = ctypes.CDLL(bsa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -160,6 +160,26 @@ def test_route_pooled_validation(kw, status, msg):
                             None)
     assert st == status, (st, L.bsa_last_error())
     assert msg in L.bsa_last_error().decode()
+
+
+def test_stripe_validation():
+    L = bsa.lib()
+    g = bsa.Grid(2, 16, 16, (4, 4, 4), 64)._c()
+    s = bsa._Shape(1, 2, 64)
+    ok = (ctypes.c_int32 * 12)(1, 0, 2, 1, 0, 3, 2, 1, 2, 3, -1, 3)
+    bad = (ctypes.c_int32 * 12)(1, 0, 2, 1, 0, 3, 3, 0, 2, 1, 0, 1)      # head 1: Tw > Ts
+    assert L.bsa_stripe_mask(bad, ctypes.byref(s), ctypes.byref(g), FAKE, FAKE, FAKE, FAKE,
+                             1 << 30, None) == -1
+    assert "head 1" in L.bsa_last_error().decode()
+    assert L.bsa_stripe_mask(None, ctypes.byref(s), ctypes.byref(g), FAKE, FAKE, FAKE, FAKE,
+                             1 << 30, None) == -1
+    assert L.bsa_stripe_mask(ok, ctypes.byref(s), ctypes.byref(g), FAKE, FAKE, FAKE, FAKE, 16,
+                             None) == -3
+    s96 = bsa._Shape(1, 2, 96)
+    assert L.bsa_stripe_mask(ok, ctypes.byref(s96), ctypes.byref(g), FAKE, FAKE, FAKE, FAKE,
+                             1 << 30, None) == -2
+    n = L.bsa_stripe_workspace_bytes(ctypes.byref(s), ctypes.byref(g))
+    assert n > 0 and n % 256 == 0
 
 
 def test_attn_validation_before_device_query():
