@@ -1,0 +1,163 @@
+"""FP8 (e4m3) attention, oracle side.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests and the bench's CPU leg, never by the product
+path; shares no code with the HIP kernels.
+
+Source: VC-Attention page ("VC-Attention: Value Smoothing and Softmax Casting for Low-bit
+Attention", abstract): a low-bit attention kernel whose two matrix products run on low-bit
+tensor cores, quantized per hardware block with a scale set by the block's largest entry, and
+whose probabilities are cast to E4M3 codes between the exponential and the second product.
+Readings used here:
+
+* E4M3 is the OCP 8-bit format with 4 exponent bits (bias 7), 3 mantissa bits, subnormals,
+  largest finite value 448 and no infinities; conversion rounds to nearest, ties to even.
+* Q and K are quantized per block of B tokens of one (batch, head): s = amax / 448 over the
+  block's B x D values, code = e4m3(x * (448 / amax)) in fp32 (a block of zeros: s = 0,
+  codes 0).  V is quantized with one scale per (batch, head) (amax over all its tokens), so
+  the second product needs no per-block rescaling.
+* The probabilities of one query row are exp(l_u - m) for the logits l_u = scale * <q, k_u>
+  of the dequantized Q and K, m the running maximum over the key blocks taken so far in the
+  row's column order, multiplied by 2^8 and cast to E4M3 (so the largest is 256, inside the
+  format's normal range); the row sum is kept unquantized.  The output is
+  (sum_u P8_u v_u) / (sum_u p_u) for the dequantized v_u.
+
+`e4m3_round` is written from the format definition and pinned against PyTorch's
+float8_e4m3fn conversion.  `attn_error_bound` bounds what casting the probabilities to E4M3
+alone can change in the output (derived below); the tests compare the GPU's FP8 attention
+with the exact fp64 attention over the dequantized inputs against that bound.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .bsa_oracle import num_blocks, padded_len, widen_bf16
+
+E4M3_MAX = 448.0
+P_OFFSET_LOG2 = 8          # probabilities are cast as 2^8 * exp(l - m)
+
+
+def e4m3_round(x) -> np.ndarray:
+    """fp32 values -> E4M3 codes (uint8), round to nearest even; |x| <= 448 expected."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)     # exact widening
+    sign = (np.signbit(x)).astype(np.uint8) << 7
+    a = np.abs(x)
+    if np.any(a > 464.0):                                       # 464 rounds past 448
+        raise ValueError("value outside the E4M3 range")
+    codes = np.zeros(a.shape, dtype=np.uint8)
+    sub = a < 2.0 ** -6
+    # subnormals: multiples of 2^-9
+    q = np.rint(a[sub] * 2.0 ** 9)                              # rint: ties to even
+    codes[sub] = q.astype(np.uint8)                             # q == 8 is the smallest normal
+    # normals: exponent e in [-6, 8], 3 mantissa bits
+    an = a[~sub]
+    e = np.floor(np.log2(an)).astype(np.int64)
+    frac = an / np.exp2(e) - 1.0                                # [0, 1)
+    mq = np.rint(frac * 8.0)
+    carry = mq >= 8
+    e = e + carry
+    mq = np.where(carry, 0, mq)
+    codes[~sub] = ((e + 7) << 3 | mq.astype(np.int64)).astype(np.uint8)
+    return codes | sign
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    v = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7))
+    if np.any((e == 0xF) & (m == 0x7)):
+        raise ValueError("NaN code")
+    return s * v
+
+
+def _scale_codes(x32, amax):
+    """codes of x32 (fp32) with the scale set by amax (fp32); returns (codes, s)."""
+    amax = np.float32(amax)
+    if amax == 0:
+        return np.zeros(x32.shape, np.uint8), np.float32(0.0)
+    inv = np.float32(np.float32(E4M3_MAX) / amax)
+    return e4m3_round(x32 * inv), np.float32(amax / np.float32(E4M3_MAX))
+
+
+def quantize_rows(xt_bits, B: int):
+    """Per-block E4M3 of tiled bf16 [b, h, Npad, D] -> (codes [b, h, Npad, D] u8,
+    scales [b, h, n_blk] f32)."""
+    x = widen_bf16(xt_bits).astype(np.float32)                  # exact
+    b, h, Np, D = x.shape
+    n = Np // B
+    codes = np.empty(x.shape, np.uint8)
+    scales = np.empty((b, h, n), np.float32)
+    for bi in range(b):
+        for hi in range(h):
+            for j in range(n):
+                blk = x[bi, hi, j * B:(j + 1) * B]
+                codes[bi, hi, j * B:(j + 1) * B], scales[bi, hi, j] = _scale_codes(
+                    blk, np.abs(blk).max())
+    return codes, scales
+
+
+def v_key_order(B: int) -> np.ndarray:
+    """Key held at byte position pos of a transposed V row: the order in which one lane of
+    the FP8 kernel holds its probabilities (64-key chunk c, half h, byte b ->
+    key 64c + 32(b // 16) + 8((b % 16) // 4) + 4h + b % 4)."""
+    pos = np.arange(B)
+    c, h, b = pos // 64, (pos % 64) // 32, pos % 32
+    return 64 * c + 32 * (b // 16) + 8 * ((b % 16) // 4) + 4 * h + b % 4
+
+
+def quantize_v(vt_bits, B: int):
+    """Per-(batch, head) E4M3 of tiled bf16 V -> (codes [b, h, n_blk, D, B] u8, each block
+    stored transposed with its keys in v_key_order, scales [b, h] f32)."""
+    x = widen_bf16(vt_bits).astype(np.float32)
+    b, h, Np, D = x.shape
+    n = Np // B
+    order = v_key_order(B)
+    codes = np.empty((b, h, n, D, B), np.uint8)
+    scales = np.empty((b, h), np.float32)
+    for bi in range(b):
+        for hi in range(h):
+            c, scales[bi, hi] = _scale_codes(x[bi, hi], np.abs(x[bi, hi]).max())
+            blocks = c.reshape(n, B, D)                          # [block, key, d]
+            codes[bi, hi] = np.transpose(blocks[:, order, :], (0, 2, 1))
+    return codes, scales
+
+
+def dequantize_rows(codes, scales, B: int) -> np.ndarray:
+    v = e4m3_decode(codes)
+    return v * np.repeat(scales.astype(np.float64), B, axis=2)[..., None]
+
+
+def dequantize_v(codes, scales, B: int) -> np.ndarray:
+    """Block-transposed V codes -> tiled [b, h, Npad, D] fp64."""
+    b, h, n, D, _ = codes.shape
+    order = v_key_order(B)
+    v = e4m3_decode(codes)                                       # [b, h, n, D, B]
+    out = np.empty((b, h, n, B, D))
+    out[:, :, :, order, :] = np.transpose(v, (0, 1, 2, 4, 3))
+    return out.reshape(b, h, n * B, D) * scales.astype(np.float64)[:, :, None, None]
+
+
+def attn_error_bound(q, k, v, row_ptr, col_idx, N: int, B: int, scale: float, rows):
+    """Per-element bound on |O_fp8 - O| for the listed rows (b, h, i) of fp64 inputs q, k, v
+    [b, h, Npad, D] (the dequantized tensors) and the exact attention O over them.
+
+    Only the probabilities are rounded: each cast value P8 = e4m3(e) of e = 2^8 exp(l - m)
+    <= 256 differs from e by at most half a unit in the last place, i.e. by
+    <= 2^-4 e (normal codes) or <= 2^-10 (subnormal codes, e < 2^-6).  The row sum L of the
+    e's is >= 2^8 (the element that set the running maximum contributes 2^8).  So
+        |dO| <= sum_u (2^-4 e_u + 2^-10) |v_u| / L <= 2^-4 sum_u w_u |v_u| + 2^-18 sum_u |v_u|
+    with w_u the exact softmax weights.  Returns {row: bound [rows of the block, D]}."""
+    n = num_blocks(N, B)
+    out = {}
+    for (bi, hi, i) in rows:
+        r = (bi * q.shape[1] + hi) * n + i
+        sel = col_idx[row_ptr[r]:row_ptr[r + 1]]
+        keys = np.concatenate([np.arange(j * B, min((j + 1) * B, N)) for j in sel])
+        lo, hi_ = i * B, min((i + 1) * B, N)
+        lg = scale * (q[bi, hi, lo:hi_] @ k[bi, hi, keys].T)
+        w = np.exp(lg - lg.max(axis=1, keepdims=True))
+        w /= w.sum(axis=1, keepdims=True)
+        av = np.abs(v[bi, hi, keys])
+        out[(bi, hi, i)] = 2.0 ** -4 * (w @ av) + 2.0 ** -18 * av.sum(axis=0)[None, :]
+    return out

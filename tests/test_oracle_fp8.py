@@ -1,0 +1,131 @@
+"""Pins of the oracle's FP8 (e4m3) pieces: the rounding against PyTorch's float8_e4m3fn
+conversion, the code table, the quantization layouts, and the probability-cast error bound
+against a brute-force simulation of the cast."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import fp8
+from oracle.bsa_oracle import num_blocks
+
+
+def test_rounding_matches_torch_float8_e4m3fn():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(50000).astype(np.float32) * s
+                        for s in (1e-4, 1e-2, 1, 30, 120)])
+    x = x[np.abs(x) <= 448]
+    bits = np.arange(0, 1 << 16, dtype=np.uint32)
+    bf = (bits << 16).view(np.float32)
+    bf = bf[np.isfinite(bf) & (np.abs(bf) <= 448)]              # every bf16 value in range
+    vals = fp8.e4m3_decode(np.arange(0, 127, dtype=np.uint8))
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)      # every tie
+    allx = np.concatenate([x, bf, mids, -mids]).astype(np.float32)
+    ref = torch.from_numpy(allx).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(fp8.e4m3_round(allx), ref)
+
+
+def test_code_table():
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    v = fp8.e4m3_decode(codes)
+    assert np.array_equal(fp8.e4m3_round(v.astype(np.float32))[v != 0], codes[v != 0])
+    assert fp8.e4m3_decode(np.uint8(0x7E)) == 448.0
+    assert fp8.e4m3_decode(np.uint8(0x01)) == 2.0 ** -9       # smallest subnormal
+    assert fp8.e4m3_decode(np.uint8(0x08)) == 2.0 ** -6       # smallest normal
+    assert fp8.e4m3_decode(np.uint8(0x38)) == 1.0
+    with pytest.raises(ValueError):
+        fp8.e4m3_round(np.float32(465.0))
+
+
+def _bf16_bits(x):
+    return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_quantize_rows_scale_and_error():
+    rng = np.random.default_rng(1)
+    B, D = 64, 64
+    x = rng.standard_normal((2, 3, 3 * B, D)) * np.array([0.01, 1.0, 50.0])[None, :, None, None]
+    x[1, 2, B:2 * B] = 0.0                                       # an all-zero block
+    bits = _bf16_bits(x)
+    xv = fp8.widen_bf16(bits)
+    codes, s = fp8.quantize_rows(bits, B)
+    assert s[1, 2, 1] == 0 and not codes[1, 2, B:2 * B].any()
+    deq = fp8.dequantize_rows(codes, s, B)
+    for bi in range(2):
+        for hi in range(3):
+            for j in range(3):
+                blk = xv[bi, hi, j * B:(j + 1) * B]
+                amax = np.abs(blk).max()
+                if amax == 0:
+                    continue
+                # the largest entry lands on the top code 448
+                assert np.abs(fp8.e4m3_decode(codes[bi, hi, j * B:(j + 1) * B])).max() == 448.0
+                assert s[bi, hi, j] == np.float32(np.float32(amax) / np.float32(448))
+                err = np.abs(deq[bi, hi, j * B:(j + 1) * B] - blk)
+                # half an ulp: 2^-4 relative (normal codes) or 2^-10 codes (subnormal)
+                assert np.all(err <= 2.0 ** -4 * np.abs(blk) * 1.0001 + 2.0 ** -10 * s[bi, hi, j])
+
+
+def test_v_layout_roundtrip():
+    rng = np.random.default_rng(2)
+    B, D = 128, 64
+    order = fp8.v_key_order(B)
+    assert sorted(order.tolist()) == list(range(B))
+    # the first 16 positions of half 0 are the keys one lane holds of the first 32-key tile
+    assert order[:16].tolist() == [8 * g + u for g in range(4) for u in range(4)]
+    assert order[32:48].tolist() == [8 * g + 4 + u for g in range(4) for u in range(4)]
+    x = rng.standard_normal((1, 2, 2 * B, D))
+    bits = _bf16_bits(x)
+    codes, s = fp8.quantize_v(bits, B)
+    assert codes.shape == (1, 2, 2, D, B)
+    # block 1, feature 3, position p holds key order[p] of block 1
+    c_rows, _ = fp8.quantize_rows(bits, 2 * B)                   # same per-head scale
+    assert np.array_equal(codes[0, 1, 1, 3], c_rows[0, 1, B + order, 3])
+    deq = fp8.dequantize_v(codes, s, B)
+    xv = fp8.widen_bf16(bits)
+    assert np.all(np.abs(deq - xv) <= 2.0 ** -4 * np.abs(xv) * 1.0001 + 2.0 ** -10 * s[:, :, None, None])
+
+
+def test_error_bound_holds_for_simulated_cast():
+    """Brute force: run the online softmax block by block in the column order with the
+    probabilities cast to E4M3 as 2^8 exp(l - m_running), and check the result against the
+    exact attention within attn_error_bound."""
+    rng = np.random.default_rng(3)
+    B, D, N = 64, 64, 5 * 64 - 7
+    n = num_blocks(N, B)
+    Np = n * B
+    q = rng.standard_normal((1, 1, Np, D)) * 1.5
+    k = rng.standard_normal((1, 1, Np, D))
+    v = rng.standard_normal((1, 1, Np, D)) * 3
+    for t in (q, k, v):
+        t[:, :, N:] = 0
+    scale = 1 / np.sqrt(D)
+    row_ptr = np.array([0, 5, 7, 10, 11, 16])
+    col_idx = np.array([0, 1, 2, 3, 4, 1, 3, 0, 2, 4, 2, 0, 1, 2, 3, 4])
+    rows = [(0, 0, i) for i in range(n)]
+    bound = fp8.attn_error_bound(q, k, v, row_ptr, col_idx, N, B, scale, rows)
+    worst = 0.0
+    for (_, _, i) in rows:
+        lo, hi = i * B, min((i + 1) * B, N)
+        acc = np.zeros((hi - lo, D))
+        lsum = np.zeros((hi - lo, 1))
+        m = np.full((hi - lo, 1), -np.inf)
+        keys_all = []
+        for j in col_idx[row_ptr[i]:row_ptr[i + 1]]:
+            keys = np.arange(j * B, min((j + 1) * B, N))
+            keys_all.append(keys)
+            lg = scale * (q[0, 0, lo:hi] @ k[0, 0, keys].T)
+            mn = np.maximum(m, lg.max(axis=1, keepdims=True))
+            a = np.exp(m - mn)
+            e = 2.0 ** 8 * np.exp(lg - mn)
+            p8 = fp8.e4m3_decode(fp8.e4m3_round(e.astype(np.float32)))
+            acc = acc * a + p8 @ v[0, 0, keys]
+            lsum = lsum * a + e.sum(axis=1, keepdims=True)
+            m = mn
+        keys = np.concatenate(keys_all)
+        lg = scale * (q[0, 0, lo:hi] @ k[0, 0, keys].T)
+        w = np.exp(lg - lg.max(axis=1, keepdims=True))
+        exact = (w / w.sum(axis=1, keepdims=True)) @ v[0, 0, keys]
+        err = np.abs(acc / lsum - exact)
+        assert np.all(err <= bound[(0, 0, i)])
+        worst = max(worst, float((err / bound[(0, 0, i)]).max()))
+    assert worst > 0.01            # the bound is not vacuous by orders of magnitude
