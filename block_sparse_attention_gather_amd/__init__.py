@@ -95,6 +95,9 @@ def _load():
         "bsa_stripe_workspace_bytes": (SZ, [S, G]),
         "bsa_stripe_mask": (I32, [P, S, G, P, P, P, P, SZ, P]),
         "bsa_attn_workspace_bytes": (SZ, [S, G]),
+        "bsa_quantize_fp8": (I32, [P, P, P, I32, S, G, P]),
+        "bsa_attn_fp8_workspace_bytes": (SZ, [S, G]),
+        "bsa_sparse_attn_fwd_fp8": (I32, [P, P, P, P, P, P, P, P, S, G, F32, P, P, P, SZ, P]),
         "bsa_sparse_attn_fwd": (I32, [P, P, P, P, P, S, G, F32, P, P, P, SZ, P]),
         "bsa_last_error": (ctypes.c_char_p, []),
         "bsa_version": (ctypes.c_char_p, []),
@@ -382,6 +385,71 @@ def sparse_attn_fwd(q_t, k_t, v_t, row_ptr, col_idx, grid: Grid,
         ctypes.byref(s), ctypes.byref(g), scale, out.data_ptr(),
         _ptr(lse) if return_lse else None, workspace.data_ptr(), workspace.numel(),
         _stream(q_t)))
+    return out, (lse if return_lse else None)
+
+
+def quantize_fp8(x_t, grid: Grid, v_layout: bool = False, out=None, scales=None):
+    """E4M3 codes of a tiled bf16 tensor [b, h, Npad, 128] -> (codes uint8, scales fp32).
+
+    v_layout=False (Q, K): codes [b, h, Npad, 128], one scale per 128-token block [b, h, n_blk];
+    v_layout=True (V): codes [b, h, n_blk, 128, 128] (blocks transposed, keys in the FP8
+    kernel's lane order), one scale per (batch, head) [b, h]."""
+    import torch
+    _require(x_t, torch.bfloat16, "x_t")
+    b, h, Np, D = x_t.shape
+    if Np != grid.Npad:
+        raise ValueError(f"x_t needs {grid.Npad} rows")
+    shape_o = (b, h, grid.n_blk, D, grid.block) if v_layout else (b, h, Np, D)
+    shape_s = (b, h) if v_layout else (b, h, grid.n_blk)
+    if out is None:
+        out = torch.empty(shape_o, dtype=torch.uint8, device=x_t.device)
+    if scales is None:
+        scales = torch.empty(shape_s, dtype=torch.float32, device=x_t.device)
+    _require(out, torch.uint8, "out")
+    _require(scales, torch.float32, "scales")
+    if tuple(out.shape) != shape_o or tuple(scales.shape) != shape_s:
+        raise ValueError(f"out must be {shape_o} and scales {shape_s}")
+    g, s = grid._c(), _shape(b, h, D)
+    _check(_load().bsa_quantize_fp8(x_t.data_ptr(), out.data_ptr(), scales.data_ptr(),
+                                    int(bool(v_layout)), ctypes.byref(s), ctypes.byref(g),
+                                    _stream(x_t)))
+    return out, scales
+
+
+def sparse_attn_fwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, row_ptr, col_idx, grid: Grid,
+                        scale: Optional[float] = None, out=None, lse=None, workspace=None,
+                        return_lse: bool = True):
+    """FP8 attention over quantize_fp8 outputs -> (out_t [b, h, Npad, 128] bf16, lse)."""
+    import torch
+    for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        _require(t, torch.uint8, n)
+    for t, n in ((q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _require(t, torch.float32, n)
+    _require(row_ptr, torch.int32, "row_ptr")
+    _require(col_idx, torch.int32, "col_idx")
+    b, h, Np, D = q8.shape
+    if tuple(k8.shape) != (b, h, Np, D) or tuple(v8.shape) != (b, h, grid.n_blk, D, grid.block):
+        raise ValueError("k8 must match q8, v8 must be [b, h, n_blk, D, B]")
+    if row_ptr.numel() != b * h * grid.n_blk + 1:
+        raise ValueError("row_ptr must have rows + 1 entries")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dev = q8.device
+    if out is None:
+        out = torch.empty((b, h, Np, D), dtype=torch.bfloat16, device=dev)
+    _require(out, torch.bfloat16, "out")
+    if return_lse and lse is None:
+        lse = torch.empty((b, h, Np), dtype=torch.float32, device=dev)
+    g, s = grid._c(), _shape(b, h, D)
+    if workspace is None:
+        n = int(_load().bsa_attn_fp8_workspace_bytes(ctypes.byref(s), ctypes.byref(g)))
+        if n == 0:
+            _check(-2)
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    _check(_load().bsa_sparse_attn_fwd_fp8(
+        q8.data_ptr(), q_scale.data_ptr(), k8.data_ptr(), k_scale.data_ptr(), v8.data_ptr(),
+        v_scale.data_ptr(), row_ptr.data_ptr(), col_idx.data_ptr(), ctypes.byref(s),
+        ctypes.byref(g), scale, out.data_ptr(), _ptr(lse) if return_lse else None,
+        workspace.data_ptr(), workspace.numel(), _stream(q8)))
     return out, (lse if return_lse else None)
 
 

@@ -247,6 +247,74 @@ bsa_status bsa_stripe_mask(const bsa_stripe* params, const bsa_shape* shape,
                          nnz, ws, (hipStream_t)stream);
 }
 
+static bsa_status check_fp8_dims(const bsa_shape* shape, const Geometry& g) {
+    bsa_status st = check_kernel_dims(shape, g);
+    if (st != BSA_OK) return st;
+    if (shape->head_dim != 128 || g.B != 128)
+        return fail(BSA_ERR_UNSUPPORTED, "the FP8 path is built for head_dim 128 and block 128");
+    return BSA_OK;
+}
+
+bsa_status bsa_quantize_fp8(const void* x_t, void* x8, float* scales, int32_t v_layout,
+                            const bsa_shape* shape, const bsa_grid* grid, void* stream) {
+    Geometry g;
+    bsa_status st = geometry(grid, &g);
+    if (st != BSA_OK) return st;
+    if ((st = check_shape(shape)) != BSA_OK) return st;
+    if (!x_t || !x8 || !scales) return fail(BSA_ERR_INVALID_ARG, "x_t/x8/scales is NULL");
+    if (v_layout != 0 && v_layout != 1)
+        return fail(BSA_ERR_INVALID_ARG, "v_layout must be 0 (Q, K) or 1 (V)");
+    if ((st = check_fp8_dims(shape, g)) != BSA_OK) return st;
+    if (((uintptr_t)x_t | (uintptr_t)x8) & 15)
+        return fail(BSA_ERR_INVALID_ARG, "x_t/x8 must be 16-byte aligned");
+    if ((uintptr_t)scales & 3) return fail(BSA_ERR_INVALID_ARG, "scales must be 4-byte aligned");
+    const int64_t n_src = (int64_t)shape->batch * shape->heads * g.Npad * shape->head_dim * 2;
+    const int64_t n_dst = n_src / 2;
+    const char* s0 = (const char*)x_t;
+    const char* d0 = (const char*)x8;
+    if (s0 < d0 + n_dst && d0 < s0 + n_src) return fail(BSA_ERR_INVALID_ARG, "x_t and x8 overlap");
+    return launch_quant_fp8(x_t, x8, scales, v_layout, shape->batch, shape->heads, g,
+                            (hipStream_t)stream);
+}
+
+size_t bsa_attn_fp8_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid) {
+    Geometry g;
+    if (geometry(grid, &g) != BSA_OK || check_shape(shape) != BSA_OK) return 0;
+    if (check_fp8_dims(shape, g) != BSA_OK) return 0;
+    DeviceInfo dev;
+    if (device_info(&dev) != BSA_OK) return 0;
+    return attn_ws_bytes(shape->batch, shape->heads, shape->head_dim, g, attn_fp8_slots(dev));
+}
+
+bsa_status bsa_sparse_attn_fwd_fp8(const void* q8, const float* q_scale, const void* k8,
+                                   const float* k_scale, const void* v8, const float* v_scale,
+                                   const int32_t* row_ptr, const int32_t* col_idx,
+                                   const bsa_shape* shape, const bsa_grid* grid, float scale,
+                                   void* out_t, float* lse, void* ws, size_t ws_bytes,
+                                   void* stream) {
+    Geometry g;
+    bsa_status st = geometry(grid, &g);
+    if (st != BSA_OK) return st;
+    if ((st = check_shape(shape)) != BSA_OK) return st;
+    if (!q8 || !q_scale || !k8 || !k_scale || !v8 || !v_scale || !row_ptr || !col_idx || !out_t)
+        return fail(BSA_ERR_INVALID_ARG, "every pointer except lse must be non-NULL");
+    if (!(scale > 0.f) || !isfinite(scale))
+        return fail(BSA_ERR_INVALID_ARG, "scale must be finite and positive");
+    if ((st = check_fp8_dims(shape, g)) != BSA_OK) return st;
+    if (((uintptr_t)q8 | (uintptr_t)k8 | (uintptr_t)v8 | (uintptr_t)out_t) & 15)
+        return fail(BSA_ERR_INVALID_ARG, "q8/k8/v8/out_t must be 16-byte aligned");
+    DeviceInfo dev;
+    if ((st = device_info(&dev)) != BSA_OK) return st;
+    const size_t need =
+        attn_ws_bytes(shape->batch, shape->heads, shape->head_dim, g, attn_fp8_slots(dev));
+    if (!ws || ws_bytes < need || ((uintptr_t)ws & 255))
+        return fail(BSA_ERR_WORKSPACE, "fp8 attention workspace: need %zu bytes, 256-byte aligned",
+                    need);
+    return launch_attn_fp8(q8, q_scale, k8, k_scale, v8, v_scale, row_ptr, col_idx,
+                           shape->batch, shape->heads, g, scale, out_t, lse, ws, dev,
+                           (hipStream_t)stream);
+}
+
 size_t bsa_attn_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid) {
     Geometry g;
     if (geometry(grid, &g) != BSA_OK || check_shape(shape) != BSA_OK) return 0;
@@ -268,7 +336,8 @@ bsa_status bsa_sparse_attn_fwd(const void* q_t, const void* k_t, const void* v_t
     if ((st = check_shape(shape)) != BSA_OK) return st;
     if (!q_t || !k_t || !v_t || !row_ptr || !col_idx || !out_t)
         return fail(BSA_ERR_INVALID_ARG, "q_t, k_t, v_t, row_ptr, col_idx, out_t must be non-NULL");
-    if (!isfinite(scale)) return fail(BSA_ERR_INVALID_ARG, "scale must be finite");
+    if (!(scale > 0.f) || !isfinite(scale))
+        return fail(BSA_ERR_INVALID_ARG, "scale must be finite and positive");
     if ((st = check_kernel_dims(shape, g)) != BSA_OK) return st;
     if ((((uintptr_t)q_t | (uintptr_t)k_t | (uintptr_t)v_t | (uintptr_t)out_t) & 15))
         return fail(BSA_ERR_INVALID_ARG, "q_t/k_t/v_t/out_t must be 16-byte aligned");

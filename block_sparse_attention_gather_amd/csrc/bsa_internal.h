@@ -60,6 +60,7 @@ struct DeviceInfo {
 bsa_status device_info(DeviceInfo* out);
 // persistent attention workgroups for one device: CUs x resident workgroups per CU
 int attn_slots(int32_t D, int32_t B, const DeviceInfo& dev);
+int attn_fp8_slots(const DeviceInfo& dev);
 int attn_max_heads();
 int attn_max_blocks();
 
@@ -91,6 +92,14 @@ bsa_status launch_attn(const void* q_t, const void* k_t, const void* v_t,
                        const int32_t* row_ptr, const int32_t* col_idx, int32_t batch,
                        int32_t heads, int32_t D, const Geometry& g, float scale, void* out_t,
                        float* lse, void* ws, const DeviceInfo& dev, hipStream_t s);
+
+bsa_status launch_attn_fp8(const void* q8, const float* qs, const void* k8, const float* ks,
+                           const void* v8, const float* vs, const int32_t* row_ptr,
+                           const int32_t* col_idx, int32_t batch, int32_t heads,
+                           const Geometry& g, float scale, void* out_t, float* lse, void* ws,
+                           const DeviceInfo& dev, hipStream_t s);
+bsa_status launch_quant_fp8(const void* x_t, void* x8, float* scales, int32_t v_layout,
+                            int32_t batch, int32_t heads, const Geometry& g, hipStream_t s);
 
 // ---- small helpers -------------------------------------------------------------------
 static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

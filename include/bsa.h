@@ -186,12 +186,47 @@ BSA_API size_t bsa_attn_workspace_bytes(const bsa_shape* shape, const bsa_grid* 
  * The heavy-row scheduler is persistent: work items are built on the device from the CSR row
  * lengths, long rows are split and their partial results merged in a fixed order, so the
  * output is bitwise deterministic.
+ * scale must be finite and > 0 (BSA_ERR_INVALID_ARG otherwise).
  * ws: device workspace of at least bsa_attn_workspace_bytes() bytes, 256-byte aligned. */
 BSA_API bsa_status bsa_sparse_attn_fwd(const void* q_t, const void* k_t, const void* v_t,
                                const int32_t* row_ptr, const int32_t* col_idx,
                                const bsa_shape* shape, const bsa_grid* grid, float scale,
                                void* out_t, float* lse, void* ws, size_t ws_bytes,
                                void* stream);
+
+/* ---- 4. FP8 (E4M3) attention (VC-Attention page, abstract) ------------------------- */
+/* Both products on FP8 matrix cores with fp32 accumulation; head_dim 128 and block 128 only
+ * (other shapes -> BSA_ERR_UNSUPPORTED).  E4M3 is the OCP 8-bit format (4 exponent bits,
+ * bias 7, 3 mantissa bits, largest finite 448); conversions round to nearest even.
+ *
+ * Quantize one tiled bf16 tensor x_t [batch, heads, Npad, 128]:
+ *   v_layout == 0 (Q, K): one scale per block of 128 tokens, scales [batch, heads, n_blk] fp32,
+ *     s = amax / 448 over the block, x8[...] = e4m3(x * (448 / amax)) in the same
+ *     [batch, heads, Npad, 128] byte layout;
+ *   v_layout == 1 (V): one scale per (batch, head), scales [batch, heads] fp32, and every block
+ *     stored transposed, x8 [batch, heads, n_blk, 128 (feature), 128 (key)] bytes, the keys of
+ *     a row in the order 64c + 32(b / 16) + 8((b % 16) / 4) + 4h + b % 4 for byte 64c + 32h + b.
+ *   A block (or head) of zeros gets scale 0 and codes 0.  x_t and x8 16-byte aligned, not
+ *   overlapping; scales 4-byte aligned. */
+BSA_API bsa_status bsa_quantize_fp8(const void* x_t, void* x8, float* scales, int32_t v_layout,
+                                    const bsa_shape* shape, const bsa_grid* grid, void* stream);
+
+/* Workspace bytes bsa_sparse_attn_fwd_fp8 needs (queries the current device); 0 if the shape
+ * is unsupported. */
+BSA_API size_t bsa_attn_fp8_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid);
+
+/* bsa_sparse_attn_fwd over the quantized tensors of bsa_quantize_fp8 (q8/k8 with per-block
+ * scales, v8 transposed with per-head scales): logits from the dequantized Q and K; the
+ * probabilities 2^8 exp(logit - m) (m the running maximum over the row's blocks in CSR
+ * order) are cast to E4M3 before the product with the dequantized V, the row sum is kept in
+ * fp32.  Outputs, CSR requirements and errors as bsa_sparse_attn_fwd; ws of at least
+ * bsa_attn_fp8_workspace_bytes() bytes. */
+BSA_API bsa_status bsa_sparse_attn_fwd_fp8(const void* q8, const float* q_scale, const void* k8,
+                                           const float* k_scale, const void* v8,
+                                           const float* v_scale, const int32_t* row_ptr,
+                                           const int32_t* col_idx, const bsa_shape* shape,
+                                           const bsa_grid* grid, float scale, void* out_t,
+                                           float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- diagnostics ------------------------------------------------------------------- */
 /* Message of the calling thread's last non-OK status ("" if none).  Valid until the next

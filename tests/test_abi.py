@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "bsa.h")
 def _declared():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(bsa_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(bsa_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_header_compiles_as_c99_and_cxx(tmp_path):
@@ -31,7 +31,7 @@ def test_header_compiles_as_c99_and_cxx(tmp_path):
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 16, names
     lib = ctypes.CDLL(bsa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n

@@ -1,0 +1,98 @@
+"""GPU tests of the FP8 (E4M3) path through the C ABI, against the oracle's FP8 reading.
+
+* Quantization: the codes and scales of bsa_quantize_fp8 are bit-identical to the oracle's
+  (per-block Q/K, per-head transposed V), including an all-zero block and a ragged tail.
+* Attention: bsa_sparse_attn_fwd_fp8 against the exact fp64 attention over the dequantized
+  inputs, per element within the bound on what casting the probabilities to E4M3 can change
+  (oracle/fp8.attn_error_bound) plus the bf16 rounding of the output; LSE within 1e-3.  One
+  routed CSR and one whose rows are split and merged.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_gather_amd as bsa
+import oracle as O
+from oracle import fp8 as F
+from workloads import Config, gen_qkv
+
+from gpu_common import attn_scale, bf16_f64, grid_of, to_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _tiled(cfg, zero_block=None):
+    q, k, v = gen_qkv(cfg, gains=np.full(cfg.heads, 1.5))
+    grid = grid_of(cfg)
+    q_t, k_t, v_t = (bsa.reorder(to_dev(x), grid) for x in (q, k, v))
+    if zero_block is not None:
+        hh, j = zero_block
+        for t in (q_t, k_t):
+            t[0, hh, j * cfg.block:(j + 1) * cfg.block] = 0
+    return grid, q_t, k_t, v_t
+
+
+def test_quantize_matches_oracle():
+    cfg = Config("f8q", 4, 12, 21, 2, 128, 128, (4, 4, 8), 0.9, 2, 81)
+    grid, q_t, k_t, v_t = _tiled(cfg, zero_block=(1, 3))
+    print(f"[gpu] fp8 quantize N={cfg.N} n_blk={grid.n_blk}", flush=True)
+    q8, qs = bsa.quantize_fp8(q_t, grid)
+    v8, vs = bsa.quantize_fp8(v_t, grid, v_layout=True)
+    torch.cuda.synchronize()
+    rc, rs = F.quantize_rows(to_bits(q_t), cfg.block)
+    assert np.array_equal(q8.cpu().numpy(), rc)
+    assert np.array_equal(qs.cpu().numpy(), rs)
+    assert rs[0, 1, 3] == 0
+    vc, vsr = F.quantize_v(to_bits(v_t), cfg.block)
+    assert np.array_equal(v8.cpu().numpy(), vc)
+    assert np.array_equal(vs.cpu().numpy(), vsr)
+
+
+@pytest.mark.parametrize("grid3,heads,routed,seed", [((4, 12, 21), 3, True, 82),
+                                                     ((6, 24, 32), 1, False, 83)],
+                         ids=["routed", "split_full"])
+def test_fp8_attention_within_bound(grid3, heads, routed, seed):
+    T, H, W = grid3
+    cfg = Config("f8a", T, H, W, heads, 128, 128, (4, 4, 8), 0.9, 2, seed)
+    grid, q_t, k_t, v_t = _tiled(cfg)
+    n, N, B = grid.n_blk, cfg.N, cfg.block
+    if routed:
+        rp, ci, nnz = bsa.score_and_route(q_t, k_t, grid, cfg.top_p, cfg.k_floor)
+    else:                                         # every row full: long rows are split
+        rp = torch.arange(0, heads * n + 1, dtype=torch.int32, device="cuda:0") * n
+        ci = torch.arange(n, dtype=torch.int32, device="cuda:0").repeat(heads * n)
+        nnz = rp[-1:]
+    q8, qs = bsa.quantize_fp8(q_t, grid)
+    k8, ks = bsa.quantize_fp8(k_t, grid)
+    v8, vs = bsa.quantize_fp8(v_t, grid, v_layout=True)
+    sc = attn_scale(128)
+    out, lse = bsa.sparse_attn_fwd_fp8(q8, qs, k8, ks, v8, vs, rp, ci, grid, sc)
+    torch.cuda.synchronize()
+    nz = int(nnz.item())
+    print(f"[gpu] fp8 attention {T}x{H}x{W} heads={heads} n_blk={n} nnz={nz}", flush=True)
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    ci_h = ci[:nz].cpu().numpy().astype(np.int64)
+    qc, qsr = F.quantize_rows(to_bits(q_t), B)
+    kc, ksr = F.quantize_rows(to_bits(k_t), B)
+    vc, vsr = F.quantize_v(to_bits(v_t), B)
+    qd, kd, vd = F.dequantize_rows(qc, qsr, B), F.dequantize_rows(kc, ksr, B), F.dequantize_v(vc, vsr, B)
+    Oref, Lref = O.sparse_attn(qd, kd, vd, rp_h, ci_h, N, B, sc)
+    rows = [(0, hh, i) for hh in range(heads) for i in range(n)]
+    bound = F.attn_error_bound(qd, kd, vd, rp_h, ci_h, N, B, sc, rows)
+    got = bf16_f64(out)
+    worst = 0.0
+    for (_, hh, i) in rows:
+        lo, hi = i * B, min((i + 1) * B, N)
+        ref = Oref[0, hh, lo:hi]
+        tol = 1.05 * bound[(0, hh, i)] + 2.0 ** -8 * np.abs(ref) + 1e-5
+        err = np.abs(got[0, hh, lo:hi] - ref)
+        assert np.all(err <= tol), (hh, i, float((err / tol).max()))
+        worst = max(worst, float((err / tol).max()))
+    dl = np.abs(lse.cpu().numpy()[:, :, :N] - Lref[:, :, :N])
+    assert dl.max() <= 1e-3
+    assert np.all(got[:, :, N:] == 0)
+    # accuracy against the exact attention on the bf16 inputs (reported, not a bar)
+    O16, _ = O.sparse_attn(to_bits(q_t), to_bits(k_t), to_bits(v_t), rp_h, ci_h, N, B, sc)
+    d16 = np.abs(got[:, :, :N] - O16[:, :, :N])
+    print(f"[gpu]   worst err/bound {worst:.3f}; vs bf16-input attention max-abs "
+          f"{d16.max():.3e} mean-abs {d16.mean():.3e}", flush=True)
