@@ -88,7 +88,8 @@ def _load():
         "bsa_num_blocks": (I32, [G]),
         "bsa_padded_len": (I32, [G]),
         "bsa_reorder": (I32, [P, P, S, G, I32, P]),
-        "bsa_reorder_pool": (I32, [P, P, P, S, G, P]),
+        "bsa_reorder_pool": (I32, [P, P, P, P, P, S, G, P]),
+        "bsa_reorder_quantize_v": (I32, [P, P, P, P, S, G, P]),
         "bsa_route_workspace_bytes": (SZ, [S, G]),
         "bsa_score_and_route": (I32, [P, P, S, G, F64, I32, F64, P, P, P, P, P, SZ, P]),
         "bsa_route_pooled": (I32, [P, P, S, G, F64, I32, F64, P, P, P, P, P, SZ, P]),
@@ -208,28 +209,69 @@ def reorder(x, grid: Grid, inverse: bool = False, out=None):
     return out
 
 
-def reorder_pool(x, grid: Grid, out=None, pooled=None):
-    """Forward reorder plus the per-block means routing pools: raster [b, N, h, D] bf16 ->
-    (tiled [b, h, Npad, D] bf16, pooled [b, h, n_blk, D] fp64), in one pass over x."""
+def reorder_pool(x, grid: Grid, out=None, pooled=None, tiled: bool = True, fp8: bool = False,
+                 x8=None, x8_scales=None):
+    """Forward reorder plus the per-block means routing pools, in one pass over raster
+    x [b, N, h, D] bf16 -> (tiled [b, h, Npad, D] bf16 or None, pooled [b, h, n_blk, D] fp64)
+    and, with fp8=True, also the E4M3 codes [b, h, Npad, D] and per-block scales
+    [b, h, n_blk] of quantize_fp8 -> (tiled, pooled, x8, x8_scales).  tiled=False skips the
+    bf16 output."""
     import torch
     _require(x, torch.bfloat16, "x")
     b, N, h, D = x.shape
     if N != grid.N:
         raise ValueError(f"x has {N} tokens, grid has {grid.N}")
-    if out is None:
-        out = torch.empty((b, h, grid.Npad, D), dtype=x.dtype, device=x.device)
-    _require(out, torch.bfloat16, "out")
-    if tuple(out.shape) != (b, h, grid.Npad, D):
-        raise ValueError(f"out must have shape {(b, h, grid.Npad, D)}")
+    dev = x.device
+    if tiled and out is None:
+        out = torch.empty((b, h, grid.Npad, D), dtype=x.dtype, device=dev)
+    if out is not None:
+        _require(out, torch.bfloat16, "out")
+        if tuple(out.shape) != (b, h, grid.Npad, D):
+            raise ValueError(f"out must have shape {(b, h, grid.Npad, D)}")
     if pooled is None:
-        pooled = torch.empty((b, h, grid.n_blk, D), dtype=torch.float64, device=x.device)
+        pooled = torch.empty((b, h, grid.n_blk, D), dtype=torch.float64, device=dev)
     _require(pooled, torch.float64, "pooled")
     if tuple(pooled.shape) != (b, h, grid.n_blk, D):
         raise ValueError(f"pooled must have shape {(b, h, grid.n_blk, D)}")
+    if fp8:
+        if x8 is None:
+            x8 = torch.empty((b, h, grid.Npad, D), dtype=torch.uint8, device=dev)
+        if x8_scales is None:
+            x8_scales = torch.empty((b, h, grid.n_blk), dtype=torch.float32, device=dev)
+        _require(x8, torch.uint8, "x8")
+        _require(x8_scales, torch.float32, "x8_scales")
     g, s = grid._c(), _shape(b, h, D)
-    _check(_load().bsa_reorder_pool(x.data_ptr(), out.data_ptr(), pooled.data_ptr(),
+    _check(_load().bsa_reorder_pool(x.data_ptr(), _ptr(out), pooled.data_ptr(),
+                                    _ptr(x8) if fp8 else None,
+                                    _ptr(x8_scales) if fp8 else None,
                                     ctypes.byref(s), ctypes.byref(g), _stream(x)))
+    if fp8:
+        return out, pooled, x8, x8_scales
     return out, pooled
+
+
+def reorder_quantize_v(x, grid: Grid, out=None, tiled: bool = False, v8=None, v_scales=None):
+    """Raster V [b, N, h, 128] bf16 -> (tiled bf16 or None, E4M3 codes [b, h, n_blk, 128, 128],
+    per-head scales [b, h]) as reorder + quantize_fp8(v_layout=True)."""
+    import torch
+    _require(x, torch.bfloat16, "x")
+    b, N, h, D = x.shape
+    if N != grid.N:
+        raise ValueError(f"x has {N} tokens, grid has {grid.N}")
+    dev = x.device
+    if tiled and out is None:
+        out = torch.empty((b, h, grid.Npad, D), dtype=x.dtype, device=dev)
+    if v8 is None:
+        v8 = torch.empty((b, h, grid.n_blk, D, grid.block), dtype=torch.uint8, device=dev)
+    if v_scales is None:
+        v_scales = torch.empty((b, h), dtype=torch.float32, device=dev)
+    _require(v8, torch.uint8, "v8")
+    _require(v_scales, torch.float32, "v_scales")
+    g, s = grid._c(), _shape(b, h, D)
+    _check(_load().bsa_reorder_quantize_v(x.data_ptr(), _ptr(out), v8.data_ptr(),
+                                          v_scales.data_ptr(), ctypes.byref(s), ctypes.byref(g),
+                                          _stream(x)))
+    return out, v8, v_scales
 
 
 def route_workspace_bytes(batch, heads, D, grid: Grid) -> int:

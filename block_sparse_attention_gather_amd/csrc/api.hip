@@ -139,28 +139,69 @@ bsa_status bsa_reorder(const void* src, void* dst, const bsa_shape* shape, const
                           (hipStream_t)stream);
 }
 
-bsa_status bsa_reorder_pool(const void* src, void* dst, double* pooled, const bsa_shape* shape,
-                            const bsa_grid* grid, void* stream) {
+static bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+    if (!a || !b) return false;
+    const char* x = (const char*)a;
+    const char* y = (const char*)b;
+    return x < y + nb && y < x + na;
+}
+
+bsa_status bsa_reorder_pool(const void* src, void* dst, double* pooled, void* x8,
+                            float* x8_scales, const bsa_shape* shape, const bsa_grid* grid,
+                            void* stream) {
     Geometry g;
     bsa_status st = geometry(grid, &g);
     if (st != BSA_OK) return st;
     if ((st = check_shape(shape)) != BSA_OK) return st;
-    if (!src || !dst || !pooled) return fail(BSA_ERR_INVALID_ARG, "src/dst/pooled is NULL");
+    if (!src) return fail(BSA_ERR_INVALID_ARG, "src is NULL");
+    if ((x8 == nullptr) != (x8_scales == nullptr))
+        return fail(BSA_ERR_INVALID_ARG, "x8 and x8_scales must be both NULL or both set");
+    if (!dst && !pooled && !x8) return fail(BSA_ERR_INVALID_ARG, "no output requested");
     if ((st = check_kernel_dims(shape, g)) != BSA_OK) return st;
-    if (((uintptr_t)src | (uintptr_t)dst) & 15)
-        return fail(BSA_ERR_INVALID_ARG, "src/dst must be 16-byte aligned");
-    if ((uintptr_t)pooled & 7) return fail(BSA_ERR_INVALID_ARG, "pooled must be 8-byte aligned");
-    const int64_t bytes_src = (int64_t)shape->batch * shape->heads * g.N * shape->head_dim * 2;
-    const int64_t bytes_dst = (int64_t)shape->batch * shape->heads * g.Npad * shape->head_dim * 2;
-    const int64_t bytes_pool = (int64_t)shape->batch * shape->heads * g.n_blk * shape->head_dim * 8;
-    const char* s0 = (const char*)src;
-    const char* d0 = (const char*)dst;
-    const char* p0 = (const char*)pooled;
-    if ((s0 < d0 + bytes_dst && d0 < s0 + bytes_src) || (s0 < p0 + bytes_pool && p0 < s0 + bytes_src) ||
-        (d0 < p0 + bytes_pool && p0 < d0 + bytes_dst))
-        return fail(BSA_ERR_INVALID_ARG, "src, dst and pooled must not overlap");
-    return launch_reorder_pool(src, dst, pooled, shape->batch, shape->heads, shape->head_dim, g,
-                               (hipStream_t)stream);
+    if (x8 && (shape->head_dim != 128 || g.B != 128))
+        return fail(BSA_ERR_UNSUPPORTED, "the FP8 path is built for head_dim 128 and block 128");
+    if (((uintptr_t)src | (uintptr_t)dst | (uintptr_t)x8) & 15)
+        return fail(BSA_ERR_INVALID_ARG, "src/dst/x8 must be 16-byte aligned");
+    if (((uintptr_t)pooled & 7) || ((uintptr_t)x8_scales & 3))
+        return fail(BSA_ERR_INVALID_ARG, "pooled must be 8-byte and x8_scales 4-byte aligned");
+    const int64_t bh = (int64_t)shape->batch * shape->heads;
+    const int64_t n_src = bh * g.N * shape->head_dim * 2;
+    const int64_t n_dst = bh * g.Npad * shape->head_dim * 2;
+    const int64_t n_pool = bh * g.n_blk * shape->head_dim * 8;
+    const int64_t n_x8 = n_dst / 2, n_sc = bh * g.n_blk * 4;
+    const void* bufs[5] = {src, dst, pooled, x8, x8_scales};
+    const int64_t lens[5] = {n_src, n_dst, n_pool, n_x8, n_sc};
+    for (int i = 0; i < 5; ++i)
+        for (int k = i + 1; k < 5; ++k)
+            if (overlap(bufs[i], lens[i], bufs[k], lens[k]))
+                return fail(BSA_ERR_INVALID_ARG, "src, dst, pooled, x8 and x8_scales must not overlap");
+    return launch_reorder_pool(src, dst, pooled, x8, x8_scales, shape->batch, shape->heads,
+                               shape->head_dim, g, (hipStream_t)stream);
+}
+
+bsa_status bsa_reorder_quantize_v(const void* src, void* dst, void* v8, float* v_scales,
+                                  const bsa_shape* shape, const bsa_grid* grid, void* stream) {
+    Geometry g;
+    bsa_status st = geometry(grid, &g);
+    if (st != BSA_OK) return st;
+    if ((st = check_shape(shape)) != BSA_OK) return st;
+    if (!src || !v8 || !v_scales) return fail(BSA_ERR_INVALID_ARG, "src/v8/v_scales is NULL");
+    if ((st = check_kernel_dims(shape, g)) != BSA_OK) return st;
+    if (shape->head_dim != 128 || g.B != 128)
+        return fail(BSA_ERR_UNSUPPORTED, "the FP8 path is built for head_dim 128 and block 128");
+    if (((uintptr_t)src | (uintptr_t)dst | (uintptr_t)v8) & 15)
+        return fail(BSA_ERR_INVALID_ARG, "src/dst/v8 must be 16-byte aligned");
+    if ((uintptr_t)v_scales & 3) return fail(BSA_ERR_INVALID_ARG, "v_scales must be 4-byte aligned");
+    const int64_t bh = (int64_t)shape->batch * shape->heads;
+    const int64_t n_src = bh * g.N * 256, n_dst = bh * g.Npad * 256;
+    const void* bufs[4] = {src, dst, v8, v_scales};
+    const int64_t lens[4] = {n_src, n_dst, n_dst / 2, bh * 4};
+    for (int i = 0; i < 4; ++i)
+        for (int k = i + 1; k < 4; ++k)
+            if (overlap(bufs[i], lens[i], bufs[k], lens[k]))
+                return fail(BSA_ERR_INVALID_ARG, "src, dst, v8 and v_scales must not overlap");
+    return launch_reorder_quant_v(src, dst, v8, v_scales, shape->batch, shape->heads, g,
+                                  (hipStream_t)stream);
 }
 
 size_t bsa_route_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid) {

@@ -48,6 +48,27 @@ static __device__ __forceinline__ uint32_t tile_pos_to_raster(uint32_t p, const 
     return (t * H + h) * W + w;
 }
 
+// bf16 words -> fp32, and eight bf16 -> eight E4M3 codes (hardware round to nearest even)
+static __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+static __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// eight bf16 -> eight E4M3 codes
+static __device__ __forceinline__ uint2 codes8(const uint4& x, float inv) {
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(bf_lo(x.x) * inv, bf_hi(x.x) * inv, 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(bf_lo(x.y) * inv, bf_hi(x.y) * inv, lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(bf_lo(x.z) * inv, bf_hi(x.z) * inv, 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(bf_lo(x.w) * inv, bf_hi(x.w) * inv, hi, true);
+    return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
+static __device__ __forceinline__ float amax8(const uint4& x) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    float m = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m = fmaxf(m, fmaxf(fabsf(bf_lo(w[q])), fabsf(bf_hi(w[q]))));
+    return m;
+}
+
 // ---- error reporting (thread-local message, see bsa_last_error) ---------------------
 bsa_status fail(bsa_status st, const char* fmt, ...);
 bsa_status check_launch(const char* what);
@@ -68,8 +89,12 @@ int attn_max_blocks();
 bsa_status launch_reorder(const void* src, void* dst, int32_t batch, int32_t heads,
                           int32_t D, const Geometry& g, int inverse, hipStream_t s);
 
-bsa_status launch_reorder_pool(const void* src, void* dst, double* pooled, int32_t batch,
-                               int32_t heads, int32_t D, const Geometry& g, hipStream_t s);
+bsa_status launch_reorder_pool(const void* src, void* dst, double* pooled, void* x8,
+                               float* x8_scales, int32_t batch, int32_t heads, int32_t D,
+                               const Geometry& g, hipStream_t s);
+bsa_status launch_reorder_quant_v(const void* src, void* dst, void* v8, float* v_scales,
+                                  int32_t batch, int32_t heads, const Geometry& g,
+                                  hipStream_t s);
 
 size_t route_ws_bytes(int32_t batch, int32_t heads, int32_t D, const Geometry& g);
 bsa_status launch_route_pooled(const double* qbar, const double* kbar, int32_t batch,

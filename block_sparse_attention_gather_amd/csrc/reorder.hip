@@ -85,18 +85,22 @@ void launch_dir(const uint4* sp, uint4* dp, const GridArgs& ga, dim3 grid, int32
 }
 
 // Forward reorder fused with routing's block pooling: workgroup (j, bh) gathers the B raster
-// rows of block j of (batch, head) bh (head_dim D contiguous elements each), writes them as
-// the contiguous tiled block (pad rows zero) and sums every column over the block's real rows
-// in fp64; pooled[bh][j] = column sums / real rows.  The sums of bf16 values are exact in
-// fp64 for the value ranges involved, so the means equal a separate pooling pass bit for bit.
-template <int D, int B>
+// rows of block j of (batch, head) bh (head_dim D contiguous elements each) and, each output
+// optional, writes them as the contiguous tiled block (pad rows zero), sums every column over
+// the block's real rows in fp64 (pooled[bh][j] = column sums / real rows; the sums of bf16
+// values are exact in fp64 for the value ranges involved, so the means equal a separate
+// pooling pass bit for bit), and with FP8 writes the block's E4M3 codes and scale exactly as
+// the per-block quantization of the tiled tensor does (amax over the block, pad rows zero).
+template <int D, int B, bool FP8>
 __global__ __launch_bounds__(kReorderThreads) void reorder_pool_kernel(
     const uint4* __restrict__ src, uint4* __restrict__ dst, double* __restrict__ pooled,
-    GridArgs g, int32_t heads, uint32_t N, uint32_t Npad) {
+    uint2* __restrict__ x8, float* __restrict__ x8_scales, GridArgs g, int32_t heads,
+    uint32_t N, uint32_t Npad) {
     constexpr int DCH = D / 8;                    // 16-byte chunks per row
     constexpr int RPP = kReorderThreads / DCH;    // rows per pass
     constexpr int NP = B / RPP;                   // passes (rows per thread)
     __shared__ double red[RPP][D + 1];
+    __shared__ float amax_red[kReorderThreads / 64];
     const int t = threadIdx.x;
     const int dc = t % DCH, rp = t / DCH;
     const uint32_t j = blockIdx.x;
@@ -115,27 +119,49 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_pool_kernel(
             v[k] = make_uint4(0, 0, 0, 0);
         }
     }
-    double acc[8];
+    if (dst) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-#pragma unroll
-    for (int k = 0; k < NP; ++k) {
-        const uint32_t p = lo + rp + RPP * k;
-        dst[((size_t)bh * Npad + p) * DCH + dc] = v[k];
-        const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            acc[2 * u] += (double)__uint_as_float(w[u] << 16);
-            acc[2 * u + 1] += (double)__uint_as_float(w[u] & 0xffff0000u);
-        }
+        for (int k = 0; k < NP; ++k) dst[((size_t)bh * Npad + lo + rp + RPP * k) * DCH + dc] = v[k];
     }
+    if (FP8) {
+        float am = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) red[rp][dc * 8 + e] = acc[e];
-    __syncthreads();
-    for (int d = t; d < D; d += kReorderThreads) {
-        double sum = 0.0;
-        for (int r = 0; r < RPP; ++r) sum += red[r][d];
-        pooled[((size_t)bh * gridDim.x + j) * D + d] = sum / (double)(hi - lo);
+        for (int k = 0; k < NP; ++k) am = fmaxf(am, amax8(v[k]));
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
+        if ((t & 63) == 0) amax_red[t >> 6] = am;
+        __syncthreads();
+        float amax = amax_red[0];
+#pragma unroll
+        for (int i = 1; i < kReorderThreads / 64; ++i) amax = fmaxf(amax, amax_red[i]);
+        const float inv = amax > 0.f ? 448.0f / amax : 0.f;
+#pragma unroll
+        for (int k = 0; k < NP; ++k)
+            x8[((size_t)bh * Npad + lo + rp + RPP * k) * DCH + dc] =
+                amax > 0.f ? codes8(v[k], inv) : make_uint2(0, 0);
+        if (t == 0) x8_scales[(size_t)bh * gridDim.x + j] = amax / 448.0f;
+    }
+    if (pooled) {
+        double acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                acc[2 * u] += (double)bf_lo(w[u]);
+                acc[2 * u + 1] += (double)bf_hi(w[u]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[rp][dc * 8 + e] = acc[e];
+        __syncthreads();
+        for (int d = t; d < D; d += kReorderThreads) {
+            double sum = 0.0;
+            for (int r = 0; r < RPP; ++r) sum += red[r][d];
+            pooled[((size_t)bh * gridDim.x + j) * D + d] = sum / (double)(hi - lo);
+        }
     }
 }
 
@@ -162,26 +188,25 @@ bsa_status launch_reorder(const void* src, void* dst, int32_t batch, int32_t hea
     return check_launch("reorder");
 }
 
-bsa_status launch_reorder_pool(const void* src, void* dst, double* pooled, int32_t batch,
-                               int32_t heads, int32_t D, const Geometry& g, hipStream_t s) {
+bsa_status launch_reorder_pool(const void* src, void* dst, double* pooled, void* x8,
+                               float* x8_scales, int32_t batch, int32_t heads, int32_t D,
+                               const Geometry& g, hipStream_t s) {
     GridArgs ga{g.T, g.H, g.W, g.tt, g.th, g.tw};
     const dim3 grid((unsigned)g.n_blk, (unsigned)(batch * heads));
     const uint4* sp = (const uint4*)src;
     uint4* dp = (uint4*)dst;
+    uint2* qp = (uint2*)x8;
     const uint32_t N = (uint32_t)g.N, Npad = (uint32_t)g.Npad;
     const dim3 blk(kReorderThreads);
-    if (D == 128 && g.B == 128)
-        hipLaunchKernelGGL((reorder_pool_kernel<128, 128>), grid, blk, 0, s, sp, dp, pooled, ga,
-                           heads, N, Npad);
-    else if (D == 128)
-        hipLaunchKernelGGL((reorder_pool_kernel<128, 64>), grid, blk, 0, s, sp, dp, pooled, ga,
-                           heads, N, Npad);
-    else if (g.B == 128)
-        hipLaunchKernelGGL((reorder_pool_kernel<64, 128>), grid, blk, 0, s, sp, dp, pooled, ga,
-                           heads, N, Npad);
-    else
-        hipLaunchKernelGGL((reorder_pool_kernel<64, 64>), grid, blk, 0, s, sp, dp, pooled, ga,
-                           heads, N, Npad);
+#define BSA_RP(DD, BB, F8)                                                                       \
+    hipLaunchKernelGGL((reorder_pool_kernel<DD, BB, F8>), grid, blk, 0, s, sp, dp, pooled, qp, \
+                       x8_scales, ga, heads, N, Npad)
+    if (x8) BSA_RP(128, 128, true);                  // the FP8 path: D = B = 128 (checked)
+    else if (D == 128 && g.B == 128) BSA_RP(128, 128, false);
+    else if (D == 128) BSA_RP(128, 64, false);
+    else if (g.B == 128) BSA_RP(64, 128, false);
+    else BSA_RP(64, 64, false);
+#undef BSA_RP
     return check_launch("reorder_pool");
 }
 

@@ -90,15 +90,29 @@ BSA_API bsa_status bsa_reorder(const void* src, void* dst, const bsa_shape* shap
                        const bsa_grid* grid, int32_t inverse, void* stream);
 
 /* Forward reorder fused with the block pooling of routing (FVAttn abstract: video-aware
- * blocks, pooled into one mean per block for the router):
- *   dst    as bsa_reorder(inverse = 0): tiled bf16 [batch, heads, Npad, D], pad rows zero;
- *   pooled fp64 [batch, heads, n_blk, D]: pooled[b][h][j] = mean of dst rows j*block ..
- *          min((j+1)*block, N) - 1 (the block's real tokens), bit-identical to the pooling
- *          inside bsa_score_and_route.
- * head_dim 64 or 128, block 64 or 128.  src and dst 16-byte aligned, pooled 8-byte aligned;
- * no two of the three may overlap (BSA_ERR_INVALID_ARG). */
-BSA_API bsa_status bsa_reorder_pool(const void* src, void* dst, double* pooled,
-                                    const bsa_shape* shape, const bsa_grid* grid, void* stream);
+ * blocks, pooled into one mean per block for the router) and, optionally, with the E4M3
+ * quantization of the FP8 path.  One pass over src (raster bf16 [batch, N, heads, D]); each
+ * output may be NULL (at least one must be set):
+ *   dst       as bsa_reorder(inverse = 0): tiled bf16 [batch, heads, Npad, D], pad rows zero;
+ *   pooled    fp64 [batch, heads, n_blk, D]: pooled[b][h][j] = mean of the tiled rows j*block ..
+ *             min((j+1)*block, N) - 1 (the block's real tokens), bit-identical to the pooling
+ *             inside bsa_score_and_route;
+ *   x8, x8_scales (both or neither): the E4M3 codes and per-block scales that
+ *             bsa_quantize_fp8(v_layout = 0) writes for the tiled tensor (head_dim 128 and
+ *             block 128 only, else BSA_ERR_UNSUPPORTED).
+ * head_dim 64 or 128, block 64 or 128.  src, dst, x8 16-byte aligned, pooled 8-byte,
+ * x8_scales 4-byte aligned; no two buffers may overlap (BSA_ERR_INVALID_ARG). */
+BSA_API bsa_status bsa_reorder_pool(const void* src, void* dst, double* pooled, void* x8,
+                                    float* x8_scales, const bsa_shape* shape,
+                                    const bsa_grid* grid, void* stream);
+
+/* Forward reorder of V fused with its E4M3 quantization (head_dim 128, block 128): v8 and
+ * v_scales exactly as bsa_quantize_fp8(v_layout = 1) writes them for the tiled V, and, when dst
+ * is not NULL, the tiled bf16 V as bsa_reorder.  Reads the raster V twice (head maxima, then
+ * codes).  Alignment and overlap rules as bsa_reorder_pool. */
+BSA_API bsa_status bsa_reorder_quantize_v(const void* src, void* dst, void* v8, float* v_scales,
+                                          const bsa_shape* shape, const bsa_grid* grid,
+                                          void* stream);
 
 /* ---- 2. routing frontend: pooled block scores, Top-p with a Top-k floor (FVAttn) ---- */
 /* Workspace bytes bsa_score_and_route needs (depends on shape and grid only). */

@@ -31,7 +31,7 @@ def test_header_compiles_as_c99_and_cxx(tmp_path):
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     lib = ctypes.CDLL(bsa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -128,17 +128,31 @@ def test_reorder_pool_validation():
     g = bsa.Grid(2, 16, 16, (4, 4, 4), 64)._c()
     s = bsa._Shape(1, 2, 64)
     far = FAKE + (1 << 28)
-    assert L.bsa_reorder_pool(FAKE, FAKE + (1 << 24), None, ctypes.byref(s), ctypes.byref(g),
+    dst = FAKE + (1 << 24)
+    assert L.bsa_reorder_pool(FAKE, None, None, None, None, ctypes.byref(s), ctypes.byref(g),
                               None) == -1
-    assert "NULL" in L.bsa_last_error().decode()
+    assert "no output" in L.bsa_last_error().decode()
     s96 = bsa._Shape(1, 2, 96)                       # the pooled path is built for 64 and 128
-    assert L.bsa_reorder_pool(FAKE, FAKE + (1 << 24), far, ctypes.byref(s96), ctypes.byref(g),
+    assert L.bsa_reorder_pool(FAKE, dst, far, None, None, ctypes.byref(s96), ctypes.byref(g),
                               None) == -2
-    assert L.bsa_reorder_pool(FAKE, FAKE + (1 << 24), FAKE + 4, ctypes.byref(s),
+    assert L.bsa_reorder_pool(FAKE, dst, FAKE + 4, None, None, ctypes.byref(s),
                               ctypes.byref(g), None) == -1        # pooled overlaps src
-    assert L.bsa_reorder_pool(FAKE, FAKE + (1 << 24), far + 4, ctypes.byref(s), ctypes.byref(g),
+    assert L.bsa_reorder_pool(FAKE, dst, far + 4, None, None, ctypes.byref(s), ctypes.byref(g),
                               None) == -1                         # pooled misaligned
     assert "aligned" in L.bsa_last_error().decode()
+    # E4M3 outputs: both or neither, and only for head_dim 128 / block 128
+    assert L.bsa_reorder_pool(FAKE, dst, far, far + (1 << 24), None, ctypes.byref(s),
+                              ctypes.byref(g), None) == -1
+    assert L.bsa_reorder_pool(FAKE, dst, far, far + (1 << 24), far + (1 << 25), ctypes.byref(s),
+                              ctypes.byref(g), None) == -2
+    assert L.bsa_reorder_quantize_v(FAKE, None, dst, far, ctypes.byref(s), ctypes.byref(g),
+                                    None) == -2
+    s128 = bsa._Shape(1, 2, 128)
+    g128 = bsa.Grid(2, 16, 16, (4, 4, 8), 128)._c()
+    assert L.bsa_reorder_quantize_v(FAKE, None, None, far, ctypes.byref(s128),
+                                    ctypes.byref(g128), None) == -1
+    assert L.bsa_reorder_quantize_v(FAKE, None, FAKE + 64, far, ctypes.byref(s128),
+                                    ctypes.byref(g128), None) == -1      # v8 overlaps src
 
 
 @pytest.mark.parametrize("kw,status,msg", [

@@ -48,6 +48,40 @@ def test_quantize_matches_oracle():
     assert np.array_equal(vs.cpu().numpy(), vsr)
 
 
+def test_fused_reorder_quantization():
+    """bsa_reorder_pool with E4M3 outputs and bsa_reorder_quantize_v: codes and scales
+    bit-identical to the oracle's quantization of the reordered tensors; the other outputs
+    unchanged (batch 2, ragged tail)."""
+    cfgs = [Config("f8f", 4, 12, 21, 2, 128, 128, (4, 4, 8), 0.9, 2, 90 + i) for i in range(2)]
+    qkv = [gen_qkv(c, gains=np.full(2, 1.5)) for c in cfgs]
+    q = np.concatenate([x[0] for x in qkv], axis=0)
+    v = np.concatenate([x[2] for x in qkv], axis=0)
+    cfg = cfgs[0]
+    grid = grid_of(cfg)
+    B = cfg.block
+    print(f"[gpu] fused fp8 reorder batch=2 N={cfg.N} n_blk={grid.n_blk}", flush=True)
+    tq, tv = to_dev(q), to_dev(v)
+    q_t, qbar, q8, qs = bsa.reorder_pool(tq, grid, fp8=True)
+    none_t, qbar2, q8b, qsb = bsa.reorder_pool(tq, grid, tiled=False, fp8=True)
+    v_t, v8, vs = bsa.reorder_quantize_v(tv, grid, tiled=True)
+    _, v8b, vsb = bsa.reorder_quantize_v(tv, grid)
+    plain_t, plain_bar = bsa.reorder_pool(tq, grid)
+    torch.cuda.synchronize()
+    assert none_t is None
+    ref_q = O.reorder(q, cfg.T, cfg.H, cfg.W, cfg.tile, B)
+    ref_v = O.reorder(v, cfg.T, cfg.H, cfg.W, cfg.tile, B)
+    assert np.array_equal(to_bits(q_t), ref_q) and np.array_equal(to_bits(v_t), ref_v)
+    assert torch.equal(qbar, plain_bar) and torch.equal(qbar2, plain_bar)
+    rc, rs = F.quantize_rows(ref_q, B)
+    for c8, sc in ((q8, qs), (q8b, qsb)):
+        assert np.array_equal(c8.cpu().numpy(), rc)
+        assert np.array_equal(sc.cpu().numpy(), rs)
+    vc, vsr = F.quantize_v(ref_v, B)
+    for c8, sc in ((v8, vs), (v8b, vsb)):
+        assert np.array_equal(c8.cpu().numpy(), vc)
+        assert np.array_equal(sc.cpu().numpy(), vsr)
+
+
 @pytest.mark.parametrize("grid3,heads,routed,seed", [((4, 12, 21), 3, True, 82),
                                                      ((6, 24, 32), 1, False, 83)],
                          ids=["routed", "split_full"])
