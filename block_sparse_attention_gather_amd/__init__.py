@@ -98,7 +98,8 @@ def _load():
         "bsa_attn_workspace_bytes": (SZ, [S, G]),
         "bsa_quantize_fp8": (I32, [P, P, P, I32, S, G, P]),
         "bsa_attn_fp8_workspace_bytes": (SZ, [S, G]),
-        "bsa_sparse_attn_fwd_fp8": (I32, [P, P, P, P, P, P, P, P, S, G, F32, P, P, P, SZ, P]),
+        "bsa_sparse_attn_fwd_fp8": (I32, [P, P, P, P, P, P, P, P, S, G, F32, I32, P, P, P, SZ,
+                                           P]),
         "bsa_sparse_attn_fwd": (I32, [P, P, P, P, P, S, G, F32, P, P, P, SZ, P]),
         "bsa_last_error": (ctypes.c_char_p, []),
         "bsa_version": (ctypes.c_char_p, []),
@@ -460,8 +461,9 @@ def quantize_fp8(x_t, grid: Grid, v_layout: bool = False, out=None, scales=None)
 
 def sparse_attn_fwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, row_ptr, col_idx, grid: Grid,
                         scale: Optional[float] = None, out=None, lse=None, workspace=None,
-                        return_lse: bool = True):
-    """FP8 attention over quantize_fp8 outputs -> (out_t [b, h, Npad, 128] bf16, lse)."""
+                        return_lse: bool = True, expcast: bool = False):
+    """FP8 attention over quantize_fp8 outputs -> (out_t [b, h, Npad, 128] bf16, lse).
+    expcast=True casts the probabilities with ExpCast (one FMA, no exponential)."""
     import torch
     for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
         _require(t, torch.uint8, n)
@@ -490,7 +492,8 @@ def sparse_attn_fwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, row_ptr, col_idx,
     _check(_load().bsa_sparse_attn_fwd_fp8(
         q8.data_ptr(), q_scale.data_ptr(), k8.data_ptr(), k_scale.data_ptr(), v8.data_ptr(),
         v_scale.data_ptr(), row_ptr.data_ptr(), col_idx.data_ptr(), ctypes.byref(s),
-        ctypes.byref(g), scale, out.data_ptr(), _ptr(lse) if return_lse else None,
+        ctypes.byref(g), scale, int(bool(expcast)), out.data_ptr(),
+        _ptr(lse) if return_lse else None,
         workspace.data_ptr(), workspace.numel(), _stream(q8)))
     return out, (lse if return_lse else None)
 

@@ -331,12 +331,13 @@ bsa_status bsa_sparse_attn_fwd_fp8(const void* q8, const float* q_scale, const v
                                    const float* k_scale, const void* v8, const float* v_scale,
                                    const int32_t* row_ptr, const int32_t* col_idx,
                                    const bsa_shape* shape, const bsa_grid* grid, float scale,
-                                   void* out_t, float* lse, void* ws, size_t ws_bytes,
-                                   void* stream) {
+                                   int32_t expcast, void* out_t, float* lse, void* ws,
+                                   size_t ws_bytes, void* stream) {
     Geometry g;
     bsa_status st = geometry(grid, &g);
     if (st != BSA_OK) return st;
     if ((st = check_shape(shape)) != BSA_OK) return st;
+    if (expcast != 0 && expcast != 1) return fail(BSA_ERR_INVALID_ARG, "expcast must be 0 or 1");
     if (!q8 || !q_scale || !k8 || !k_scale || !v8 || !v_scale || !row_ptr || !col_idx || !out_t)
         return fail(BSA_ERR_INVALID_ARG, "every pointer except lse must be non-NULL");
     if (!(scale > 0.f) || !isfinite(scale))
@@ -352,8 +353,8 @@ bsa_status bsa_sparse_attn_fwd_fp8(const void* q8, const float* q_scale, const v
         return fail(BSA_ERR_WORKSPACE, "fp8 attention workspace: need %zu bytes, 256-byte aligned",
                     need);
     return launch_attn_fp8(q8, q_scale, k8, k_scale, v8, v_scale, row_ptr, col_idx,
-                           shape->batch, shape->heads, g, scale, out_t, lse, ws, dev,
-                           (hipStream_t)stream);
+                           shape->batch, shape->heads, g, scale, expcast, out_t, lse, ws,
+                           dev, (hipStream_t)stream);
 }
 
 size_t bsa_attn_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid) {

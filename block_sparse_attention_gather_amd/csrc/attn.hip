@@ -762,7 +762,14 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
 // product (element e of lane L: row 8(e/4) + 4(L/32) + e mod 4, column L mod 32), so
 // S^T = K Q^T leaves each lane one query and 16 keys per 32-key tile exactly as in the bf16
 // kernel.  Probabilities are 2^8 exp(l - m) with m the exact running maximum (rescaled as soon
-// as it grows), so every cast value lies in (0, 256]; the row sum is kept unquantized.
+// as it grows), so every cast value lies in (0, 256].  Two casts:
+//   XC = false: exp2 in fp32, then E4M3 with round to nearest even; the row sum is the fp32
+//               sum of the uncast values;
+//   XC = true:  ExpCast (VC-Attention page, abstract: log-domain scores mapped to E4M3 codes
+//               by one fused multiply-add): the code of 2^y is about 8y + 56 (exponent field
+//               above the 3 mantissa bits, linear mantissa), so code = u8(8(s c - m + 8) + 56)
+//               with no exponential; the row sum is taken by two more MFMAs against an
+//               all-ones V tile, so it sums exactly the cast values.
 // ---------------------------------------------------------------------------------------
 struct AttnF8Args {
     const uint8_t* q;       // [bh][Npad][128] e4m3
@@ -837,6 +844,7 @@ __device__ __forceinline__ f32x16 mfma_f8(const v8i32& a, const v8i32& b, const 
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+template <bool XC>
 __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnF8Args a) {
     constexpr int D = 128, B = 128;
     __shared__ __align__(1024) uint8_t Ks[B * kF8Row];
@@ -899,11 +907,13 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnF8Args a) {
                 for (int u = 0; u < kF8TI; ++u) dma8_part(k0, ks_addr, wv, lane, u);
             }
 
-            f32x16 o[4];
+            f32x16 o[4], ol;
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ol[r] = 0.f;
             float m = -INFINITY, l = 0.f;
 
             for (int32_t e = it.y; e < it.z; ++e) {
@@ -967,27 +977,39 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnF8Args a) {
                     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+                    if (XC)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) ol[r] *= alpha;
                     m = mn;
                 }
                 // probabilities 2^8 exp2(s c - m), cast to E4M3; bytes 16t + e of chunk kc are
                 // element e of key tile 2 kc + t
                 v8i32 pf[2];
                 const float off = 8.0f - m;
+                const float c8 = 8.0f * c_blk, k8 = 8.0f * off + 56.0f;
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
                     for (int w = 0; w < 8; ++w) {
                         const int tt = 2 * kc + (w >> 2);
                         const int r0 = 4 * (w & 3);
-                        float p4[4];
+                        if (XC) {
+                            uint32_t pk = 0;
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            p4[j] = __builtin_amdgcn_exp2f(fmaf(s[tt][r0 + j], c_blk, off));
-                            l += p4[j];
+                            for (int j = 0; j < 4; ++j)
+                                pk = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[tt][r0 + j], c8, k8), j, pk);
+                            pf[kc][w] = (int)pk;
+                        } else {
+                            float p4[4];
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                p4[j] = __builtin_amdgcn_exp2f(fmaf(s[tt][r0 + j], c_blk, off));
+                                l += p4[j];
+                            }
+                            int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], 0, false);
+                            pk = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], pk, true);
+                            pf[kc][w] = pk;
                         }
-                        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], 0, false);
-                        pk = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], pk, true);
-                        pf[kc][w] = pk;
                     }
                 // O^T += V^T P^T: 4 feature tiles x 2 chunks of 64 keys
                 {
@@ -996,10 +1018,18 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnF8Args a) {
                     for (int i = 0; i < 8; ++i) vf[i] = f8_frag(vs_lds, 32 * (i >> 1) + l32, 2 * (i & 1) + half);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) o[i >> 1] = mfma_f8(vf[i], pf[i & 1], o[i >> 1]);
+                    if (XC) {
+                        v8i32 ones;
+#pragma unroll
+                        for (int w = 0; w < 8; ++w) ones[w] = 0x38383838;     // E4M3 1.0
+                        ol = mfma_f8(ones, pf[0], ol);
+                        ol = mfma_f8(ones, pf[1], ol);
+                    }
                 }
             }
 
-            const float lt = l + other_half(l);
+            // (ExpCast: every row of the all-ones product holds the lane's query's sum)
+            const float lt = XC ? ol[0] : l + other_half(l);
             const int64_t qpos = qrow0 + l32;
             if (it.w < 0) {
                 const float inv = lt > 0.f ? vscale / lt : 0.f;
@@ -1073,9 +1103,13 @@ int occupancy() {
 }
 
 int occupancy_fp8() {
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_fp8_kernel, 256, 0) != hipSuccess)
+    int nb = 0, nx = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_fp8_kernel<false>, 256, 0) !=
+            hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nx, attn_fp8_kernel<true>, 256, 0) !=
+            hipSuccess)
         return 1;
+    nb = nb < nx ? nb : nx;                      // one workspace size serves both casts
     return nb < 1 ? 1 : nb;
 }
 
@@ -1146,8 +1180,8 @@ bsa_status launch_attn(const void* q_t, const void* k_t, const void* v_t,
 bsa_status launch_attn_fp8(const void* q8, const float* qs, const void* k8, const float* ks,
                            const void* v8, const float* vs, const int32_t* row_ptr,
                            const int32_t* col_idx, int32_t batch, int32_t heads,
-                           const Geometry& g, float scale, void* out_t, float* lse, void* ws,
-                           const DeviceInfo& dev, hipStream_t s) {
+                           const Geometry& g, float scale, int32_t expcast, void* out_t,
+                           float* lse, void* ws, const DeviceInfo& dev, hipStream_t s) {
     const int slots = attn_fp8_slots(dev);
     const AttnLayout L = attn_layout(batch, heads, 128, g, slots);
     unsigned char* w = (unsigned char*)ws;
@@ -1186,7 +1220,10 @@ bsa_status launch_attn_fp8(const void* q8, const float* qs, const void* k8, cons
     a.Npad = g.Npad;
     a.n_blk = g.n_blk;
     a.scale_log2 = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL(attn_fp8_kernel, dim3(slots), dim3(256), 0, s, a);
+    if (expcast)
+        hipLaunchKernelGGL(attn_fp8_kernel<true>, dim3(slots), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(attn_fp8_kernel<false>, dim3(slots), dim3(256), 0, s, a);
     return check_launch("sparse_attn_fp8");
 }
 

@@ -121,8 +121,8 @@ bsa_status launch_attn(const void* q_t, const void* k_t, const void* v_t,
 bsa_status launch_attn_fp8(const void* q8, const float* qs, const void* k8, const float* ks,
                            const void* v8, const float* vs, const int32_t* row_ptr,
                            const int32_t* col_idx, int32_t batch, int32_t heads,
-                           const Geometry& g, float scale, void* out_t, float* lse, void* ws,
-                           const DeviceInfo& dev, hipStream_t s);
+                           const Geometry& g, float scale, int32_t expcast, void* out_t,
+                           float* lse, void* ws, const DeviceInfo& dev, hipStream_t s);
 bsa_status launch_quant_fp8(const void* x_t, void* x8, float* scales, int32_t v_layout,
                             int32_t batch, int32_t heads, const Geometry& g, hipStream_t s);
 

@@ -232,15 +232,23 @@ BSA_API size_t bsa_attn_fp8_workspace_bytes(const bsa_shape* shape, const bsa_gr
 /* bsa_sparse_attn_fwd over the quantized tensors of bsa_quantize_fp8 (q8/k8 with per-block
  * scales, v8 transposed with per-head scales): logits from the dequantized Q and K; the
  * probabilities 2^8 exp(logit - m) (m the running maximum over the row's blocks in CSR
- * order) are cast to E4M3 before the product with the dequantized V, the row sum is kept in
- * fp32.  Outputs, CSR requirements and errors as bsa_sparse_attn_fwd; ws of at least
- * bsa_attn_fp8_workspace_bytes() bytes. */
+ * order) are cast to E4M3 before the product with the dequantized V.
+ *   expcast == 0: exp in fp32, then round to nearest even; the row sum is the fp32 sum of the
+ *                 uncast probabilities;
+ *   expcast == 1: ExpCast (VC-Attention page, abstract): the code is 8 y + 56 for the log2
+ *                 probability y, converted to an unsigned byte, with no exponential (each
+ *                 cast value is 0.917-1.109x the probability, or within 2^-6 of it below
+ *                 2^-6); the row sum is the sum of the cast values, so the output is their
+ *                 normalized average and lse is biased by up to ln 1.109.
+ * Outputs, CSR requirements and errors as bsa_sparse_attn_fwd (expcast not 0 or 1 ->
+ * BSA_ERR_INVALID_ARG); ws of at least bsa_attn_fp8_workspace_bytes() bytes. */
 BSA_API bsa_status bsa_sparse_attn_fwd_fp8(const void* q8, const float* q_scale, const void* k8,
                                            const float* k_scale, const void* v8,
                                            const float* v_scale, const int32_t* row_ptr,
                                            const int32_t* col_idx, const bsa_shape* shape,
-                                           const bsa_grid* grid, float scale, void* out_t,
-                                           float* lse, void* ws, size_t ws_bytes, void* stream);
+                                           const bsa_grid* grid, float scale,
+                                           int32_t expcast, void* out_t, float* lse, void* ws,
+                                           size_t ws_bytes, void* stream);
 
 /* ---- diagnostics ------------------------------------------------------------------- */
 /* Message of the calling thread's last non-OK status ("" if none).  Valid until the next

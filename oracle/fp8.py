@@ -161,3 +161,60 @@ def attn_error_bound(q, k, v, row_ptr, col_idx, N: int, B: int, scale: float, ro
         av = np.abs(v[bi, hi, keys])
         out[(bi, hi, i)] = 2.0 ** -4 * (w @ av) + 2.0 ** -18 * av.sum(axis=0)[None, :]
     return out
+
+
+# ---------------------------------------------------------------------------------------
+# ExpCast (VC-Attention page, abstract: log-domain scores mapped straight to E4M3 codes with
+# one fused multiply-add, no exponential)
+# ---------------------------------------------------------------------------------------
+EXPCAST_DELTA = 2.0 ** 0.1475 - 1.0      # largest relative deviation of a cast value (below)
+EXPCAST_ABS = 2.0 ** -6                  # absolute deviation bound below the normal range
+
+
+def expcast_codes(y, rounding: str = "nearest") -> np.ndarray:
+    """Codes for log2 probabilities y (the 2^8-scaled probability is 2^y, y <= 8): the E4M3
+    code of 2^y has exponent field floor(y) + 7 above 3 mantissa bits, and taking the mantissa
+    linear in the fraction of y gives the code 8y + 56 (its exponent-field part is exact).
+    Converted to an unsigned byte, clamped to [0, 255], by rounding to nearest (ties to even)
+    or by truncation (rounding="floor")."""
+    t = 8.0 * np.asarray(y, dtype=np.float64) + 56.0
+    t = np.where(np.isnan(t), 0.0, t)
+    r = np.rint(t) if rounding == "nearest" else np.floor(t)
+    return np.clip(r, 0, 255).astype(np.uint8)
+
+
+def expcast_error_bound(q, k, v, row_ptr, col_idx, N: int, B: int, scale: float, rows):
+    """Per-element bounds (on |O_expcast - O| and on |lse_expcast - lse|) for the listed rows.
+
+    For an integer code c = 8E + M taken for t = 8y + 56 with t - c = r in [-1/2, 1) (either
+    rounding), the cast value 2^(E-7)(1 + M/8) differs from 2^y by log2 of
+    (log2(1 + M/8) - M/8) - r/8, in [-1/8, 0.085 + 1/16]: a factor in
+    [2^-0.125, 2^0.1475], so within EXPCAST_DELTA relatively.  Below 2^-6 the codes are
+    subnormal (value c 2^-9) and both values lie in [0, 2^-6]: within EXPCAST_ABS.  Every
+    error is then scaled by the rescale factors (<= 1) into the frame of the final maximum, where
+    the probabilities are e_u = 2^8 exp(l_u - max l) with sum L >= 2^8.  The output is the
+    average weighted by the cast values P8_u = e_u + eps_u and normalized by their own sum
+    (L + sum eps), so
+        |dO| <= [sum |eps_u| |v_u| + (sum |eps_u|) sum w_u |v_u|] / (L - sum |eps_u|)
+    with |eps_u| <= DELTA e_u + ABS and w_u = e_u / L, and |dlse| <= max(-ln(1 - E), ln(1 + E))
+    for E = sum |eps| / L.  Returns {row: (bound on O [rows, D], bound on lse [rows])}."""
+    n = num_blocks(N, B)
+    d, A = EXPCAST_DELTA, EXPCAST_ABS
+    out = {}
+    for (bi, hi, i) in rows:
+        r = (bi * q.shape[1] + hi) * n + i
+        sel = col_idx[row_ptr[r]:row_ptr[r + 1]]
+        keys = np.concatenate([np.arange(j * B, min((j + 1) * B, N)) for j in sel])
+        lo, hi_ = i * B, min((i + 1) * B, N)
+        lg = scale * (q[bi, hi, lo:hi_] @ k[bi, hi, keys].T)
+        e = 2.0 ** 8 * np.exp(lg - lg.max(axis=1, keepdims=True))
+        L = e.sum(axis=1, keepdims=True)
+        av = np.abs(v[bi, hi, keys])
+        W = (e / L) @ av                                  # sum w |v|
+        S = av.sum(axis=0)[None, :]                       # sum |v|
+        eps_sum = d * L + A * len(keys)
+        bo = (d * L * W + A * S + eps_sum * W) / (L - eps_sum)
+        E = (eps_sum / L)[:, 0]
+        bl = np.maximum(-np.log(np.maximum(1.0 - E, 1e-300)), np.log(1.0 + E))
+        out[(bi, hi, i)] = (bo, bl)
+    return out

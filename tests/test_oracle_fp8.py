@@ -129,3 +129,59 @@ def test_error_bound_holds_for_simulated_cast():
         assert np.all(err <= bound[(0, 0, i)])
         worst = max(worst, float((err / bound[(0, 0, i)]).max()))
     assert worst > 0.01            # the bound is not vacuous by orders of magnitude
+
+
+@pytest.mark.parametrize("rounding", ["nearest", "floor"])
+def test_expcast_codes_and_bound(rounding):
+    """ExpCast codes: exact powers of two map to their E4M3 codes; and a brute-force online
+    softmax with the probabilities cast by ExpCast (either rounding of the byte conversion)
+    stays within expcast_error_bound, output and lse."""
+    y = np.arange(-6, 9, dtype=np.float64)                    # 2^y, normal range
+    ref = torch.from_numpy((2.0 ** y).astype(np.float32)).to(torch.float8_e4m3fn)
+    assert np.array_equal(fp8.expcast_codes(y, rounding), ref.view(torch.uint8).numpy())
+    assert fp8.expcast_codes(np.array([-np.inf]), rounding)[0] == 0
+    rng = np.random.default_rng(4)
+    B, D, N = 64, 64, 6 * 64 - 5
+    n = num_blocks(N, B)
+    Np = n * B
+    q = rng.standard_normal((1, 1, Np, D)) * 2.0
+    k = rng.standard_normal((1, 1, Np, D))
+    v = rng.standard_normal((1, 1, Np, D)) * 3
+    for t in (q, k, v):
+        t[:, :, N:] = 0
+    scale = 1 / np.sqrt(D)
+    row_ptr = np.array([0, 6, 8, 11, 12, 16, 19])
+    col_idx = np.array([0, 1, 2, 3, 4, 5, 1, 3, 0, 2, 4, 2, 0, 1, 2, 3, 5, 4, 3])
+    rows = [(0, 0, i) for i in range(n)]
+    bound = fp8.expcast_error_bound(q, k, v, row_ptr, col_idx, N, B, scale, rows)
+    worst = 0.0
+    for (_, _, i) in rows:
+        lo, hi = i * B, min((i + 1) * B, N)
+        acc = np.zeros((hi - lo, D))
+        lsum = np.zeros((hi - lo, 1))
+        m = np.full((hi - lo, 1), -np.inf)
+        keys_all = []
+        for j in col_idx[row_ptr[i]:row_ptr[i + 1]]:
+            keys = np.arange(j * B, min((j + 1) * B, N))
+            keys_all.append(keys)
+            lg = scale * (q[0, 0, lo:hi] @ k[0, 0, keys].T)
+            mn = np.maximum(m, lg.max(axis=1, keepdims=True))
+            a = np.exp(m - mn)
+            y = (lg - mn) / np.log(2) + 8                      # log2 of 2^8 exp(l - m)
+            p8 = fp8.e4m3_decode(fp8.expcast_codes(y, rounding))
+            acc = acc * a + p8 @ v[0, 0, keys]
+            lsum = lsum * a + p8.sum(axis=1, keepdims=True)
+            m = mn
+        keys = np.concatenate(keys_all)
+        lg = scale * (q[0, 0, lo:hi] @ k[0, 0, keys].T)
+        mx = lg.max(axis=1, keepdims=True)
+        w = np.exp(lg - mx)
+        exact = (w / w.sum(axis=1, keepdims=True)) @ v[0, 0, keys]
+        lse = (mx + np.log(w.sum(axis=1, keepdims=True)))[:, 0]
+        lse_cast = (m[:, 0] + np.log(lsum[:, 0] / 2.0 ** 8))
+        bo, bl = bound[(0, 0, i)]
+        err = np.abs(acc / lsum - exact)
+        assert np.all(err <= bo)
+        assert np.all(np.abs(lse_cast - lse) <= bl)
+        worst = max(worst, float((err / bo).max()))
+    assert worst > 0.01
