@@ -23,7 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbsa.so")
 TRACE_LIB = os.path.join(PKG, "libbsa_trace.so")
-SOURCES = ["api.hip", "reorder.hip", "route.hip", "attn.hip", "fp8.hip"]
+SOURCES = ["api.hip", "reorder.hip", "route.hip", "attn.hip", "attn_fp8.hip", "fp8.hip"]
 ARCH = os.environ.get("BSA_OFFLOAD_ARCH", "gfx950")
 
 CFLAGS = [
