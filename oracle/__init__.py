@@ -9,3 +9,4 @@ from .bsa_oracle import (widen_bf16, num_blocks, padded_len, tile_perm, tile_per
                          masked_dense_attn, dense_attn_raster, block_mask_dense, layer)
 from .check import check_mask, check_row, compare_out, MaskReport, OutReport
 from .stripe import block_coords, stripe_keep, stripe_mask
+from .hilbert import cube_bits, hilbert_index, hilbert_order, hilbert_perm

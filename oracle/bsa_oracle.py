@@ -91,22 +91,24 @@ def tile_perm_by_sort(T: int, H: int, W: int, tile) -> np.ndarray:
     return pi.astype(np.int64)
 
 
-def reorder(x, T: int, H: int, W: int, tile, B: int) -> np.ndarray:
-    """[batch, N, heads, D] raster -> [batch, heads, Npad, D] tile order; pad rows are 0."""
+def reorder(x, T: int, H: int, W: int, tile, B: int, pi=None) -> np.ndarray:
+    """[batch, N, heads, D] raster -> [batch, heads, Npad, D] tile order (or the token order
+    pi[n] = position of raster token n, e.g. the Hilbert order); pad rows are 0."""
     x = np.asarray(x)
     b, N, h, D = x.shape
     assert N == T * H * W
-    pi = tile_perm(T, H, W, tile)
+    pi = tile_perm(T, H, W, tile) if pi is None else np.asarray(pi)
     out = np.zeros((b, h, padded_len(N, B), D), dtype=x.dtype)
     out[:, :, pi, :] = np.transpose(x, (0, 2, 1, 3))
     return out
 
 
-def inverse_reorder(xt, T: int, H: int, W: int, tile) -> np.ndarray:
-    """[batch, heads, Npad, D] tile order -> [batch, N, heads, D] raster; pad rows dropped."""
+def inverse_reorder(xt, T: int, H: int, W: int, tile, pi=None) -> np.ndarray:
+    """[batch, heads, Npad, D] tile (or pi) order -> [batch, N, heads, D] raster; pad rows
+    dropped."""
     xt = np.asarray(xt)
     N = T * H * W
-    pi = tile_perm(T, H, W, tile)
+    pi = tile_perm(T, H, W, tile) if pi is None else np.asarray(pi)
     return np.ascontiguousarray(np.transpose(xt[:, :, pi, :], (0, 2, 1, 3)))
 
 

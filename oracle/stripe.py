@@ -31,11 +31,13 @@ def check_params(p):
     return Tw, To, Ts, Sw, So, Ss
 
 
-def block_coords(T: int, H: int, W: int, tile, B: int):
-    """(bt, bs) of every block: the tile coordinates of the block's first token."""
+def block_coords(T: int, H: int, W: int, tile, B: int, pi=None):
+    """(bt, bs) of every block: the tile coordinates of the block's first token (blocks of the
+    3D-tile order, or of the token order pi[n] = position of raster token n)."""
     tt, th, tw = tile
     N = T * H * W
-    order = np.argsort(tile_perm(T, H, W, tile))       # order[pos] = raster token at pos
+    pi = tile_perm(T, H, W, tile) if pi is None else np.asarray(pi)
+    order = np.argsort(pi)                              # order[pos] = raster token at pos
     first = order[np.arange(num_blocks(N, B)) * B]
     t, h, w = first // (H * W), (first // W) % H, first % W
     nW = -(-W // tw)
@@ -50,9 +52,9 @@ def stripe_keep(bt, bs, p) -> np.ndarray:
     return (np.mod(dt, Ts) < Tw) & (np.mod(ds, Ss) < Sw)
 
 
-def stripe_mask(T: int, H: int, W: int, tile, B: int, params, batch: int = 1):
+def stripe_mask(T: int, H: int, W: int, tile, B: int, params, batch: int = 1, pi=None):
     """CSR (row_ptr, col_idx) over rows (b, h, i) for params[h] = (Tw, To, Ts, Sw, So, Ss)."""
-    bt, bs = block_coords(T, H, W, tile, B)
+    bt, bs = block_coords(T, H, W, tile, B, pi)
     counts, cols = [], []
     for _ in range(batch):
         for p in params:
