@@ -15,7 +15,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
-from dataclasses import dataclass
+from dataclasses import dataclass, field
 from typing import Optional, Tuple
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +36,8 @@ class BsaError(RuntimeError):
 class _Grid(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("W", ctypes.c_int32),
                 ("tile_t", ctypes.c_int32), ("tile_h", ctypes.c_int32),
-                ("tile_w", ctypes.c_int32), ("block", ctypes.c_int32)]
+                ("tile_w", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("order", ctypes.c_void_p)]
 
 
 class _Shape(ctypes.Structure):
@@ -46,12 +47,18 @@ class _Shape(ctypes.Structure):
 
 @dataclass(frozen=True)
 class Grid:
-    """Latent grid T x H x W, 3D tile extent and block size (tokens per block)."""
+    """Latent grid T x H x W, 3D tile extent and block size (tokens per block); `order`
+    (optional int32 GPU tensor of N entries, e.g. hilbert_order(grid)) replaces the 3D-tile
+    token order."""
     T: int
     H: int
     W: int
     tile: Tuple[int, int, int]
     block: int
+    order: Optional[object] = field(default=None, compare=False, hash=False, repr=False)
+
+    def with_order(self, order) -> "Grid":
+        return Grid(self.T, self.H, self.W, tuple(self.tile), self.block, order)
 
     @property
     def N(self) -> int:
@@ -67,7 +74,7 @@ class Grid:
 
     def _c(self) -> _Grid:
         return _Grid(self.T, self.H, self.W, self.tile[0], self.tile[1], self.tile[2],
-                     self.block)
+                     self.block, None if self.order is None else self.order.data_ptr())
 
 
 _lib = None
@@ -86,6 +93,8 @@ def _load():
     G, S = ctypes.POINTER(_Grid), ctypes.POINTER(_Shape)
     sigs = {
         "bsa_num_blocks": (I32, [G]),
+        "bsa_hilbert_order_workspace_bytes": (SZ, [G]),
+        "bsa_hilbert_order": (I32, [G, P, P, SZ, P]),
         "bsa_padded_len": (I32, [G]),
         "bsa_reorder": (I32, [P, P, S, G, I32, P]),
         "bsa_reorder_pool": (I32, [P, P, P, P, P, S, G, P]),
@@ -273,6 +282,19 @@ def reorder_quantize_v(x, grid: Grid, out=None, tiled: bool = False, v8=None, v_
                                           v_scales.data_ptr(), ctypes.byref(s), ctypes.byref(g),
                                           _stream(x)))
     return out, v8, v_scales
+
+
+def hilbert_order(grid: Grid, device="cuda:0"):
+    """Hilbert-curve token order of the grid as an int32 tensor of N entries (order[p] = raster
+    token at position p); use it with grid.with_order(...)."""
+    import torch
+    g = grid._c()
+    n = int(_load().bsa_hilbert_order_workspace_bytes(ctypes.byref(g)))
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+    order = torch.empty(grid.N, dtype=torch.int32, device=device)
+    _check(_load().bsa_hilbert_order(ctypes.byref(g), order.data_ptr(), ws.data_ptr(), ws.numel(),
+                                     _stream(order)))
+    return order
 
 
 def route_workspace_bytes(batch, heads, D, grid: Grid) -> int:

@@ -65,6 +65,8 @@ static bsa_status geometry(const bsa_grid* grid, Geometry* g) {
     g->T = grid->T; g->H = grid->H; g->W = grid->W;
     g->tt = grid->tile_t; g->th = grid->tile_h; g->tw = grid->tile_w;
     g->B = grid->block;
+    g->order = grid->order;
+    if ((uintptr_t)grid->order & 3) return fail(BSA_ERR_INVALID_ARG, "grid order must be 4-byte aligned");
     g->N = (int64_t)grid->T * grid->H * grid->W;
     if (g->N > ((int64_t)1 << 31) - 1) return fail(BSA_ERR_INVALID_ARG, "N = T*H*W exceeds int32");
     const int64_t nb = (g->N + g->B - 1) / g->B;
@@ -355,6 +357,30 @@ bsa_status bsa_sparse_attn_fwd_fp8(const void* q8, const float* q_scale, const v
     return launch_attn_fp8(q8, q_scale, k8, k_scale, v8, v_scale, row_ptr, col_idx,
                            shape->batch, shape->heads, g, scale, expcast, out_t, lse, ws,
                            dev, (hipStream_t)stream);
+}
+
+size_t bsa_hilbert_order_workspace_bytes(const bsa_grid* grid) {
+    Geometry g;
+    if (geometry(grid, &g) != BSA_OK) return 0;
+    return hilbert_ws_bytes(g);
+}
+
+bsa_status bsa_hilbert_order(const bsa_grid* grid, int32_t* order, void* ws, size_t ws_bytes,
+                             void* stream) {
+    Geometry g;
+    bsa_status st = geometry(grid, &g);
+    if (st != BSA_OK) return st;
+    if (!order) return fail(BSA_ERR_INVALID_ARG, "order is NULL");
+    if ((uintptr_t)order & 3) return fail(BSA_ERR_INVALID_ARG, "order must be 4-byte aligned");
+    if (g.order && (const int32_t*)order == g.order)
+        return fail(BSA_ERR_INVALID_ARG, "order must not be the grid's own order table");
+    int32_t side = 1;
+    while (side < g.T || side < g.H || side < g.W) side <<= 1;
+    if (side > 256) return fail(BSA_ERR_UNSUPPORTED, "the Hilbert order supports axes up to 256");
+    const size_t need = hilbert_ws_bytes(g);
+    if (!ws || ws_bytes < need || ((uintptr_t)ws & 255))
+        return fail(BSA_ERR_WORKSPACE, "hilbert workspace: need %zu bytes, 256-byte aligned", need);
+    return launch_hilbert_order(g, order, ws, (hipStream_t)stream);
 }
 
 size_t bsa_attn_workspace_bytes(const bsa_shape* shape, const bsa_grid* grid) {

@@ -15,17 +15,20 @@ struct Geometry {
     int64_t N;        // real tokens
     int32_t n_blk;    // ceil(N / B)
     int64_t Npad;     // n_blk * B
+    const int32_t* order;   // device table: raster token at each position (NULL: 3D tiles)
 };
 
 // 3D-tile grid as kernel arguments, and the tile-order position -> raster token map that
 // the reorder and the stripe-mask kernels share.
 struct GridArgs {
     int32_t T, H, W, tt, th, tw;
+    const int32_t* order;   // raster token at each position, or NULL for the 3D-tile order
 };
 
 // Tile-order position p -> raster token n, in 32-bit arithmetic (N < 2^31 is checked on the
 // host, so every intermediate fits).
 static __device__ __forceinline__ uint32_t tile_pos_to_raster(uint32_t p, const GridArgs& g) {
+    if (g.order) return (uint32_t)g.order[p];          // a caller-built order (Hilbert)
     const uint32_t T = g.T, H = g.H, W = g.W, tt = g.tt, th = g.th, tw = g.tw;
     const uint32_t slab = tt * H * W;
     const uint32_t it = p / slab;
@@ -111,6 +114,11 @@ size_t stripe_ws_bytes(int32_t batch, int32_t heads, const Geometry& g);
 bsa_status launch_stripe(const int32_t* params_host, int32_t batch, int32_t heads,
                          const Geometry& g, int32_t* row_ptr, int32_t* col_idx, int32_t* nnz,
                          void* ws, hipStream_t s);
+
+size_t hilbert_ws_bytes(const Geometry& g);
+bsa_status launch_hilbert_order(const Geometry& g, int32_t* order, void* ws, hipStream_t s);
+bsa_status launch_scan(const int32_t* counts, int32_t* excl, int32_t* total, int64_t n,
+                       hipStream_t s);
 
 size_t attn_ws_bytes(int32_t batch, int32_t heads, int32_t D, const Geometry& g, int slots);
 bsa_status launch_attn(const void* q_t, const void* k_t, const void* v_t,

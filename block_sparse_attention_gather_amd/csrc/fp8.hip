@@ -164,7 +164,7 @@ bsa_status launch_quant_fp8(const void* x_t, void* x8, float* scales, int32_t v_
                            (int64_t)g.Npad);
         return check_launch("quantize rows");
     }
-    const Gather ga{GridArgs{g.T, g.H, g.W, g.tt, g.th, g.tw}, heads, (uint32_t)g.N,
+    const Gather ga{GridArgs{g.T, g.H, g.W, g.tt, g.th, g.tw, g.order}, heads, (uint32_t)g.N,
                     (uint32_t)g.Npad};
     uint32_t* hm = (uint32_t*)scales;             // head maxima, then scales, in place
     hipLaunchKernelGGL(zero_kernel, dim3((bh + 255) / 256), dim3(256), 0, s, hm, bh);
@@ -189,7 +189,7 @@ bsa_status launch_reorder_quant_v(const void* src, void* dst, void* v8, float* v
     const int32_t bh = batch * heads;
     const dim3 grid((unsigned)g.n_blk, (unsigned)bh);
     const uint4* x = (const uint4*)src;
-    const Gather ga{GridArgs{g.T, g.H, g.W, g.tt, g.th, g.tw}, heads, (uint32_t)g.N,
+    const Gather ga{GridArgs{g.T, g.H, g.W, g.tt, g.th, g.tw, g.order}, heads, (uint32_t)g.N,
                     (uint32_t)g.Npad};
     uint32_t* hm = (uint32_t*)v_scales;
     hipLaunchKernelGGL(zero_kernel, dim3((bh + 255) / 256), dim3(256), 0, s, hm, bh);

@@ -165,11 +165,84 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_pool_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Hilbert-curve token order (DFSAttn page, abstract: tokens reordered along a Hilbert curve so
+// that blocks of consecutive tokens are compact).  Tokens are ordered by their index on the 3D
+// Hilbert curve of the smallest 2^bits cube holding the grid, axes (t, h, w), computed with
+// J. Skilling's transform ("Programming the Hilbert curve", 2004): per level from the top,
+// undo the excess work (invert the low bits of axis 0, or exchange them with axis i), then a
+// Gray code across the axes and a final correction give the transposed index, whose bits are
+// interleaved from the top level down.  The order table is built by marking the cube cells the
+// grid occupies, an exclusive scan over the cube in curve order, and placing every token at
+// the scan value of its cell.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t hilbert_index3(uint32_t t, uint32_t h, uint32_t w,
+                                                   int bits) {
+    uint32_t X[3] = {t, h, w};
+    const uint32_t M = 1u << (bits - 1);
+    for (uint32_t Q = M; Q > 1; Q >>= 1) {
+        const uint32_t P = Q - 1;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            if (X[i] & Q) {
+                X[0] ^= P;
+            } else {
+                const uint32_t x = (X[0] ^ X[i]) & P;
+                X[0] ^= x;
+                X[i] ^= x;
+            }
+        }
+    }
+    X[1] ^= X[0];
+    X[2] ^= X[1];
+    uint32_t tc = 0;
+    for (uint32_t Q = M; Q > 1; Q >>= 1)
+        if (X[2] & Q) tc ^= Q - 1;
+    X[0] ^= tc;
+    X[1] ^= tc;
+    X[2] ^= tc;
+    uint32_t idx = 0;
+    for (int b = bits - 1; b >= 0; --b)
+#pragma unroll
+        for (int i = 0; i < 3; ++i) idx = (idx << 1) | ((X[i] >> b) & 1u);
+    return idx;
+}
+
+__device__ __forceinline__ uint32_t token_hilbert(uint32_t n, const GridArgs& g, int bits) {
+    const uint32_t HW = (uint32_t)g.H * (uint32_t)g.W;
+    const uint32_t t = n / HW, r = n - t * HW;
+    const uint32_t h = r / (uint32_t)g.W, w = r - h * (uint32_t)g.W;
+    return hilbert_index3(t, h, w, bits);
+}
+
+__global__ void fill_zero_kernel(int32_t* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+__global__ void hilbert_mark_kernel(int32_t* cells, GridArgs g, uint32_t N, int bits) {
+    const uint32_t n = blockIdx.x * blockDim.x + threadIdx.x;
+    if (n < N) cells[token_hilbert(n, g, bits)] = 1;
+}
+
+__global__ void hilbert_place_kernel(const int32_t* excl, int32_t* order, GridArgs g, uint32_t N,
+                                     int bits) {
+    const uint32_t n = blockIdx.x * blockDim.x + threadIdx.x;
+    if (n < N) order[excl[token_hilbert(n, g, bits)]] = (int32_t)n;
+}
+
+static int hilbert_bits(const Geometry& g) {
+    int bits = 1;
+    while ((1 << bits) < g.T || (1 << bits) < g.H || (1 << bits) < g.W) ++bits;
+    return bits;
+}
+
 }  // namespace
 
 bsa_status launch_reorder(const void* src, void* dst, int32_t batch, int32_t heads, int32_t D,
                           const Geometry& g, int inverse, hipStream_t s) {
-    GridArgs ga{g.T, g.H, g.W, g.tt, g.th, g.tw};
+    GridArgs ga{g.T, g.H, g.W, g.tt, g.th, g.tw, g.order};
     const int64_t npos = inverse ? g.N : g.Npad;
     if (npos == 0 || batch == 0) return BSA_OK;
     const int64_t waves_per_block = kReorderThreads / 64;
@@ -191,7 +264,7 @@ bsa_status launch_reorder(const void* src, void* dst, int32_t batch, int32_t hea
 bsa_status launch_reorder_pool(const void* src, void* dst, double* pooled, void* x8,
                                float* x8_scales, int32_t batch, int32_t heads, int32_t D,
                                const Geometry& g, hipStream_t s) {
-    GridArgs ga{g.T, g.H, g.W, g.tt, g.th, g.tw};
+    GridArgs ga{g.T, g.H, g.W, g.tt, g.th, g.tw, g.order};
     const dim3 grid((unsigned)g.n_blk, (unsigned)(batch * heads));
     const uint4* sp = (const uint4*)src;
     uint4* dp = (uint4*)dst;
@@ -208,6 +281,32 @@ bsa_status launch_reorder_pool(const void* src, void* dst, double* pooled, void*
     else BSA_RP(64, 64, false);
 #undef BSA_RP
     return check_launch("reorder_pool");
+}
+
+size_t hilbert_ws_bytes(const Geometry& g) {
+    const size_t cells = (size_t)1 << (3 * hilbert_bits(g));
+    return align_up(cells * 4, 256) + align_up((cells + 1) * 4, 256) + 256;
+}
+
+bsa_status launch_hilbert_order(const Geometry& g, int32_t* order, void* ws, hipStream_t s) {
+    const int bits = hilbert_bits(g);
+    const int64_t cells = (int64_t)1 << (3 * bits);
+    unsigned char* w = (unsigned char*)ws;
+    int32_t* mark = (int32_t*)w;
+    int32_t* excl = (int32_t*)(w + align_up((size_t)cells * 4, 256));
+    int32_t* total = (int32_t*)(w + align_up((size_t)cells * 4, 256) +
+                                align_up((size_t)(cells + 1) * 4, 256));
+    const GridArgs ga{g.T, g.H, g.W, g.tt, g.th, g.tw, nullptr};   // raster coordinates only
+    const uint32_t N = (uint32_t)g.N;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(256), 0, s, mark, cells);
+    bsa_status st = check_launch("hilbert (clear)");
+    if (st != BSA_OK) return st;
+    const dim3 tg((N + 255) / 256);
+    hipLaunchKernelGGL(hilbert_mark_kernel, tg, dim3(256), 0, s, mark, ga, N, bits);
+    if ((st = check_launch("hilbert (mark)")) != BSA_OK) return st;
+    if ((st = launch_scan(mark, excl, total, cells, s)) != BSA_OK) return st;
+    hipLaunchKernelGGL(hilbert_place_kernel, tg, dim3(256), 0, s, excl, order, ga, N, bits);
+    return check_launch("hilbert (place)");
 }
 
 }  // namespace bsa

@@ -812,7 +812,7 @@ bsa_status launch_stripe(const int32_t* params_host, int32_t batch, int32_t head
         hipSuccess)
         return fail(BSA_ERR_HIP, "stripe parameters: copy to the workspace failed");
     a.params = params;
-    a.g = GridArgs{g.T, g.H, g.W, g.tt, g.th, g.tw};
+    a.g = GridArgs{g.T, g.H, g.W, g.tt, g.th, g.tw, g.order};
     a.B = g.B;
     a.n_blk = g.n_blk;
     a.heads = heads;
@@ -832,6 +832,12 @@ bsa_status launch_stripe(const int32_t* params_host, int32_t batch, int32_t head
     hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, s,
                        a.bitmap, row_ptr, col_idx, rows, nwords);
     return check_launch("fill");
+}
+
+bsa_status launch_scan(const int32_t* counts, int32_t* excl, int32_t* total, int64_t n,
+                       hipStream_t s) {
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, counts, excl, total, n);
+    return check_launch("scan");
 }
 
 }  // namespace bsa

@@ -64,11 +64,17 @@ typedef enum {
 /* Latent grid and block organization.  Tiles are visited in (it, ih, iw) order, the last tile
  * along an axis is truncated to what is left of the grid, and tokens inside a tile are
  * row-major (t, h, w).  Blocks are `block` consecutive tokens of that order.  The tile volume
- * need not equal `block` (a block may then straddle tiles). */
+ * need not equal `block` (a block may then straddle tiles).
+ * `order` replaces that token order when not NULL: a DEVICE table of N int32, order[p] = the
+ * raster token at position p (a permutation of 0..N-1, not checked), e.g. the Hilbert-curve
+ * order of bsa_hilbert_order; every call that maps positions to tokens (the reorders, the
+ * fused quantization, the stripe masks' block coordinates) then uses it.  4-byte aligned.
+ * Zero-initialising the struct's trailing members keeps the 3D-tile order. */
 typedef struct {
     int32_t T, H, W;                  /* latent grid, N = T*H*W real tokens            */
     int32_t tile_t, tile_h, tile_w;   /* 3D tile extent, each >= 1                     */
     int32_t block;                    /* tokens per block: 64 or 128                   */
+    const int32_t* order;             /* optional token order table (device), or NULL  */
 } bsa_grid;
 
 typedef struct {
@@ -113,6 +119,18 @@ BSA_API bsa_status bsa_reorder_pool(const void* src, void* dst, double* pooled, 
 BSA_API bsa_status bsa_reorder_quantize_v(const void* src, void* dst, void* v8, float* v_scales,
                                           const bsa_shape* shape, const bsa_grid* grid,
                                           void* stream);
+
+/* Hilbert-curve token order (DFSAttn page, abstract: tokens reordered along a Hilbert curve
+ * so blocks of consecutive tokens are compact).  Writes order[N] (device int32): the tokens of
+ * the T x H x W grid sorted by their index on the 3D Hilbert curve of the smallest 2^b cube
+ * holding the grid (axes t, h, w; J. Skilling's construction, "Programming the Hilbert curve",
+ * 2004), cells outside the grid skipped.  Built on the device (mark, scan, place), enqueued on
+ * stream; ws of at least bsa_hilbert_order_workspace_bytes() bytes (8^b cells x 8 bytes),
+ * 256-byte aligned.  Axes above 256 -> BSA_ERR_UNSUPPORTED.  The grid's own `order` and tile
+ * extents are ignored. */
+BSA_API size_t bsa_hilbert_order_workspace_bytes(const bsa_grid* grid);
+BSA_API bsa_status bsa_hilbert_order(const bsa_grid* grid, int32_t* order, void* ws,
+                                     size_t ws_bytes, void* stream);
 
 /* ---- 2. routing frontend: pooled block scores, Top-p with a Top-k floor (FVAttn) ---- */
 /* Workspace bytes bsa_score_and_route needs (depends on shape and grid only). */

@@ -31,7 +31,7 @@ def test_header_compiles_as_c99_and_cxx(tmp_path):
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     lib = ctypes.CDLL(bsa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -194,6 +194,22 @@ def test_stripe_validation():
                              1 << 30, None) == -2
     n = L.bsa_stripe_workspace_bytes(ctypes.byref(s), ctypes.byref(g))
     assert n > 0 and n % 256 == 0
+
+
+def test_hilbert_order_validation():
+    L = bsa.lib()
+    g = bsa.Grid(21, 30, 52, (4, 4, 8), 128)._c()
+    n = L.bsa_hilbert_order_workspace_bytes(ctypes.byref(g))
+    assert n >= 2 * 64 ** 3 * 4 and n % 256 == 0              # cube of side 64
+    assert L.bsa_hilbert_order(ctypes.byref(g), None, FAKE, n, None) == -1
+    assert L.bsa_hilbert_order(ctypes.byref(g), FAKE + 2, FAKE, n, None) == -1
+    assert L.bsa_hilbert_order(ctypes.byref(g), FAKE, FAKE, 16, None) == -3
+    big = bsa.Grid(2, 300, 16, (4, 4, 8), 128)._c()
+    assert L.bsa_hilbert_order(ctypes.byref(big), FAKE, FAKE, 1 << 40, None) == -2
+    # a misaligned order table in a grid is rejected by every call
+    bad = bsa.Grid(2, 16, 16, (4, 4, 4), 64)._c()
+    bad.order = FAKE + 2
+    assert L.bsa_num_blocks(ctypes.byref(bad)) == 0
 
 
 def test_attn_validation_before_device_query():
