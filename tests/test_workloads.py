@@ -25,6 +25,19 @@ def test_deterministic_bytes(golden_dir):
         assert _sha(gen_qkv(CONFIGS[name], threads=1)) == want[name], name
 
 
+def test_full_layer_heads_deterministic(golden_dir):
+    """Two heads of each full-size layer, byte for byte (the field uses no BLAS and no
+    vectorised math routine, so these bytes are the same on any CPU and thread count)."""
+    with open(os.path.join(golden_dir, "gen_sha256.json")) as fh:
+        want = json.load(fh)
+    keys = [k for k in want if ":heads=" in k]
+    assert len(keys) == 3
+    for key in keys:
+        name, heads = key.split(":heads=")
+        heads = [int(x) for x in heads.split(",")]
+        assert _sha(gen_qkv(CONFIGS[name], heads=heads)) == want[key], key
+
+
 def test_head_subset_matches_full():
     cfg = CONFIGS["small"]
     full = gen_qkv(cfg)

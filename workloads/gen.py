@@ -17,7 +17,11 @@ single head can be regenerated without the others):
   0..15 of K and g_h*beta*u_n to Q, u_n = [cos, sin](2 pi f h / H), [cos, sin](2 pi f w / W)
   for f = 1..4, beta = 0.7 sqrt(D / 8) (the stripe peak equals the field peak); the term has
   no t, so it repeats every frame, and it repeats every W raster positions;
-* all arithmetic in fp64, then one round-to-nearest-even to bf16; layout [1, N, heads, D].
+* all arithmetic in fp64, then one round-to-nearest-even to bf16; layout [1, N, heads, D];
+* the cosines and sines come from per-axis tables of the C library's scalar cos/sin joined by
+  the angle-addition formulas, and the products with A are elementwise sums in a fixed order,
+  so the bytes are the same on every machine and for any thread count (no BLAS, no vectorised
+  math routines).
 
 The gain g_h is the single sparsity knob (the softmax scale is fixed by the method).  Frozen
 per-config gains live in gains.json next to this file; they are produced once by a
@@ -118,9 +122,10 @@ def f64_from_bf16_bits(u) -> np.ndarray:
 # ---------------------------------------------------------------------------------------
 # generator
 # ---------------------------------------------------------------------------------------
-def _coords(cfg: Config) -> np.ndarray:
-    t, h, w = np.meshgrid(np.arange(cfg.T), np.arange(cfg.H), np.arange(cfg.W), indexing="ij")
-    return np.stack([t.ravel(), h.ravel(), w.ravel()], axis=1).astype(np.float64)  # [N, 3]
+def _axis_index(cfg: Config):
+    """Integer (t, h, w) of every raster token, each [N]."""
+    n = np.arange(cfg.N, dtype=np.int64)
+    return n // (cfg.H * cfg.W), (n // cfg.W) % cfg.H, n % cfg.W
 
 
 def _head_rng(cfg: Config, head: int) -> np.random.Generator:
@@ -128,22 +133,55 @@ def _head_rng(cfg: Config, head: int) -> np.random.Generator:
                                                                       spawn_key=(head,))))
 
 
-def _field(rng: np.random.Generator, coords: np.ndarray, sigma: float, D: int) -> np.ndarray:
+def _phasor(step: float, count: int, phase: float = 0.0):
+    """cos and sin of step*i + phase for i < count, from the C library's scalar routines."""
+    args = [step * i + phase for i in range(count)]
+    return (np.array([math.cos(a) for a in args]), np.array([math.sin(a) for a in args]))
+
+
+def _field(rng: np.random.Generator, cfg: Config, sigma: float, D: int) -> np.ndarray:
+    """A [cos(omega . c_n + phi), sin(omega . c_n + phi)] / sqrt(8) over the raster grid.
+
+    Built so that every value is a fixed sequence of single IEEE operations: per axis the
+    scalar cos/sin of that axis' term (the phase rides on t), joined by the angle-addition
+    formulas, and the mixing by A as 16 elementwise products summed in index order.  No BLAS
+    call and no vectorised transcendental routine is involved, so the bytes do not depend on
+    the CPU, the BLAS build or the number of threads."""
     omega = rng.normal(0.0, sigma, size=(8, 3))
     phi = rng.uniform(0.0, 2.0 * math.pi, size=8)
     A = rng.standard_normal((D, 16))
-    arg = coords @ omega.T + phi                                   # [N, 8]
-    z = np.concatenate([np.cos(arg), np.sin(arg)], axis=1)         # [N, 16]
-    return (z @ A.T) / math.sqrt(8.0)                              # [N, D]
+    N = cfg.N
+    z = np.empty((N, 16))
+    for m in range(8):
+        ct, st = _phasor(float(omega[m, 0]), cfg.T, float(phi[m]))
+        ch, sh = _phasor(float(omega[m, 1]), cfg.H)
+        cw, sw = _phasor(float(omega[m, 2]), cfg.W)
+        c2 = ct[:, None] * ch[None, :] - st[:, None] * sh[None, :]          # [T, H]
+        s2 = ct[:, None] * sh[None, :] + st[:, None] * ch[None, :]
+        c3 = c2[:, :, None] * cw[None, None, :] - s2[:, :, None] * sw[None, None, :]
+        s3 = c2[:, :, None] * sw[None, None, :] + s2[:, :, None] * cw[None, None, :]
+        z[:, m] = c3.reshape(N)
+        z[:, 8 + m] = s3.reshape(N)
+    f = np.zeros((N, D))
+    R = 2048                                       # rows per pass: the partial sums stay in cache
+    tmp = np.empty((R, D))
+    for r0 in range(0, N, R):
+        r1 = min(N, r0 + R)
+        fr, tr = f[r0:r1], tmp[:r1 - r0]
+        for j in range(16):
+            np.multiply(z[r0:r1, j:j + 1], A[None, :, j], out=tr)
+            np.add(fr, tr, out=fr)
+    f /= math.sqrt(8.0)
+    return f
 
 
 def _stripe_basis(cfg: Config) -> np.ndarray:
-    c = _coords(cfg)
-    hh, ww = c[:, 1], c[:, 2]
+    _, hh, ww = _axis_index(cfg)
     cols = []
     for f in range(1, 5):
-        cols += [np.cos(2 * math.pi * f * hh / cfg.H), np.sin(2 * math.pi * f * hh / cfg.H),
-                 np.cos(2 * math.pi * f * ww / cfg.W), np.sin(2 * math.pi * f * ww / cfg.W)]
+        ch, sh = _phasor(2 * math.pi * f / cfg.H, cfg.H)
+        cw, sw = _phasor(2 * math.pi * f / cfg.W, cfg.W)
+        cols += [ch[hh], sh[hh], cw[ww], sw[ww]]
     return np.stack(cols, axis=1)                                   # [N, 16]
 
 
@@ -152,14 +190,13 @@ def head_sigma(cfg: Config, rng: np.random.Generator) -> float:
     return cfg.sigma0 * (2.0 ** u) if cfg.per_head_sigma else cfg.sigma0
 
 
-def gen_head_f64(cfg: Config, head: int, gain: float = 1.0, coords=None, stripe=None):
+def gen_head_f64(cfg: Config, head: int, gain: float = 1.0, stripe=None):
     """One head's (Q, K, V) in fp64, [N, D] each, before the bf16 rounding."""
     D = cfg.head_dim
-    coords = _coords(cfg) if coords is None else coords
     rng = _head_rng(cfg, head)
     s = head_sigma(cfg, rng)
-    f = _field(rng, coords, s, D)
-    fv = _field(rng, coords, s, D)
+    f = _field(rng, cfg, s, D)
+    fv = _field(rng, cfg, s, D)
     eq = rng.standard_normal((cfg.N, D))
     ek = rng.standard_normal((cfg.N, D))
     ev = rng.standard_normal((cfg.N, D))
@@ -183,13 +220,12 @@ def gen_qkv(cfg: Config, heads: Optional[Sequence[int]] = None,
     heads = list(range(cfg.heads)) if heads is None else list(heads)
     gains = load_gains(cfg) if gains is None else np.asarray(gains, dtype=np.float64)
     N, D = cfg.N, cfg.head_dim
-    coords = _coords(cfg)
     stripe = _stripe_basis(cfg) if cfg.stripes else None
     out = [np.empty((1, N, len(heads), D), dtype=np.uint16) for _ in range(3)]
 
     def one(slot_head):
         slot, hd = slot_head
-        qkv = gen_head_f64(cfg, hd, float(gains[hd]), coords, stripe)
+        qkv = gen_head_f64(cfg, hd, float(gains[hd]), stripe)
         for t in range(3):
             out[t][0, :, slot, :] = bf16_bits_from_f64(qkv[t])
 
