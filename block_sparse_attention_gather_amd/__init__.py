@@ -220,12 +220,12 @@ def reorder(x, grid: Grid, inverse: bool = False, out=None):
 
 
 def reorder_pool(x, grid: Grid, out=None, pooled=None, tiled: bool = True, fp8: bool = False,
-                 x8=None, x8_scales=None):
+                 x8=None, x8_scales=None, pool: bool = True):
     """Forward reorder plus the per-block means routing pools, in one pass over raster
     x [b, N, h, D] bf16 -> (tiled [b, h, Npad, D] bf16 or None, pooled [b, h, n_blk, D] fp64)
     and, with fp8=True, also the E4M3 codes [b, h, Npad, D] and per-block scales
     [b, h, n_blk] of quantize_fp8 -> (tiled, pooled, x8, x8_scales).  tiled=False skips the
-    bf16 output."""
+    bf16 output; pool=False skips the block means (pooled is then None; needs another output)."""
     import torch
     _require(x, torch.bfloat16, "x")
     b, N, h, D = x.shape
@@ -238,11 +238,14 @@ def reorder_pool(x, grid: Grid, out=None, pooled=None, tiled: bool = True, fp8: 
         _require(out, torch.bfloat16, "out")
         if tuple(out.shape) != (b, h, grid.Npad, D):
             raise ValueError(f"out must have shape {(b, h, grid.Npad, D)}")
-    if pooled is None:
-        pooled = torch.empty((b, h, grid.n_blk, D), dtype=torch.float64, device=dev)
-    _require(pooled, torch.float64, "pooled")
-    if tuple(pooled.shape) != (b, h, grid.n_blk, D):
-        raise ValueError(f"pooled must have shape {(b, h, grid.n_blk, D)}")
+    if not pool:
+        pooled = None
+    else:
+        if pooled is None:
+            pooled = torch.empty((b, h, grid.n_blk, D), dtype=torch.float64, device=dev)
+        _require(pooled, torch.float64, "pooled")
+        if tuple(pooled.shape) != (b, h, grid.n_blk, D):
+            raise ValueError(f"pooled must have shape {(b, h, grid.n_blk, D)}")
     if fp8:
         if x8 is None:
             x8 = torch.empty((b, h, grid.Npad, D), dtype=torch.uint8, device=dev)
@@ -251,7 +254,7 @@ def reorder_pool(x, grid: Grid, out=None, pooled=None, tiled: bool = True, fp8: 
         _require(x8, torch.uint8, "x8")
         _require(x8_scales, torch.float32, "x8_scales")
     g, s = grid._c(), _shape(b, h, D)
-    _check(_load().bsa_reorder_pool(x.data_ptr(), _ptr(out), pooled.data_ptr(),
+    _check(_load().bsa_reorder_pool(x.data_ptr(), _ptr(out), _ptr(pooled),
                                     _ptr(x8) if fp8 else None,
                                     _ptr(x8_scales) if fp8 else None,
                                     ctypes.byref(s), ctypes.byref(g), _stream(x)))
@@ -520,13 +523,48 @@ def sparse_attn_fwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, row_ptr, col_idx,
     return out, (lse if return_lse else None)
 
 
-def layer(q, k, v, grid: Grid, top_p: float, k_floor: int, scale: Optional[float] = None):
+def layer(q, k, v, grid: Grid, top_p: float, k_floor: int, scale: Optional[float] = None,
+          mask=None):
     """Whole path on raster [b, N, h, D] bf16 inputs -> (out [b, N, h, D], row_ptr, col_idx,
-    nnz)."""
-    q_t, qbar = reorder_pool(q, grid)
-    k_t, kbar = reorder_pool(k, grid)
-    v_t = reorder(v, grid)
-    row_ptr, col_idx, nnz = route_pooled(qbar, kbar, grid, top_p, k_floor, scale)
+    nnz).  mask = (row_ptr, col_idx, nnz) of an earlier call on the same grid and shape reuses
+    that CSR: the block pooling and the routing are skipped and only the reorders and the
+    attention run (mask reuse across denoising steps)."""
+    if mask is None:
+        q_t, qbar = reorder_pool(q, grid)
+        k_t, kbar = reorder_pool(k, grid)
+        v_t = reorder(v, grid)
+        row_ptr, col_idx, nnz = route_pooled(qbar, kbar, grid, top_p, k_floor, scale)
+    else:
+        row_ptr, col_idx, nnz = mask
+        b, _, h, _ = q.shape
+        if row_ptr.numel() != b * h * grid.n_blk + 1:
+            raise ValueError(f"mask row_ptr has {row_ptr.numel()} entries, this call needs "
+                             f"{b * h * grid.n_blk + 1}")
+        q_t, k_t, v_t = reorder(q, grid), reorder(k, grid), reorder(v, grid)
     out_t, _ = sparse_attn_fwd(q_t, k_t, v_t, row_ptr, col_idx, grid, scale,
                                return_lse=False)
     return reorder(out_t, grid, inverse=True), row_ptr, col_idx, nnz
+
+
+class MaskReuse:
+    """Mask reuse across denoising steps (DFSAttn page, abstract: sparse masks are cached
+    between steps): the first call of every `interval` consecutive calls routes, the others
+    reuse its CSR.  interval = 1 routes every call.  Host-side bookkeeping only; each call runs
+    `layer`."""
+
+    def __init__(self, interval: int):
+        if int(interval) < 1:
+            raise ValueError("interval must be >= 1")
+        self.interval = int(interval)
+        self.calls = 0
+        self.mask = None
+
+    def layer(self, q, k, v, grid: Grid, top_p: float, k_floor: int,
+              scale: Optional[float] = None):
+        """-> (out, routed): `routed` says whether this call computed a new mask."""
+        routed = self.mask is None or self.calls % self.interval == 0
+        out, row_ptr, col_idx, nnz = layer(q, k, v, grid, top_p, k_floor, scale,
+                                           mask=None if routed else self.mask)
+        self.mask = (row_ptr, col_idx, nnz)
+        self.calls += 1
+        return out, routed

@@ -190,16 +190,20 @@ def head_sigma(cfg: Config, rng: np.random.Generator) -> float:
     return cfg.sigma0 * (2.0 ** u) if cfg.per_head_sigma else cfg.sigma0
 
 
-def gen_head_f64(cfg: Config, head: int, gain: float = 1.0, stripe=None):
-    """One head's (Q, K, V) in fp64, [N, D] each, before the bf16 rounding."""
+def _components(cfg: Config, rng: np.random.Generator, sigma: float):
+    """The random parts of one head, in stream order: Q/K field, V field, noise of Q, K, V."""
     D = cfg.head_dim
-    rng = _head_rng(cfg, head)
-    s = head_sigma(cfg, rng)
-    f = _field(rng, cfg, s, D)
-    fv = _field(rng, cfg, s, D)
+    f = _field(rng, cfg, sigma, D)
+    fv = _field(rng, cfg, sigma, D)
     eq = rng.standard_normal((cfg.N, D))
     ek = rng.standard_normal((cfg.N, D))
     ev = rng.standard_normal((cfg.N, D))
+    return f, fv, eq, ek, ev
+
+
+def _compose(cfg: Config, comps, gain: float, stripe):
+    f, fv, eq, ek, ev = comps
+    D = cfg.head_dim
     q = gain * (0.7 * f + 0.3 * eq)
     k = 0.7 * f + 0.3 * ek
     v = 0.7 * fv + 0.3 * ev
@@ -209,6 +213,13 @@ def gen_head_f64(cfg: Config, head: int, gain: float = 1.0, stripe=None):
         q[:, :16] += gain * beta * u
         k[:, :16] += beta * u
     return q, k, v
+
+
+def gen_head_f64(cfg: Config, head: int, gain: float = 1.0, stripe=None):
+    """One head's (Q, K, V) in fp64, [N, D] each, before the bf16 rounding."""
+    rng = _head_rng(cfg, head)
+    s = head_sigma(cfg, rng)
+    return _compose(cfg, _components(cfg, rng, s), gain, stripe)
 
 
 def gen_qkv(cfg: Config, heads: Optional[Sequence[int]] = None,
@@ -239,3 +250,61 @@ def gen_qkv(cfg: Config, heads: Optional[Sequence[int]] = None,
         for j in jobs:
             one(j)
     return out[0], out[1], out[2]
+
+
+# ---------------------------------------------------------------------------------------
+# denoising-step drift (for mask reuse across steps)
+# ---------------------------------------------------------------------------------------
+def gen_qkv_steps(cfg: Config, steps: Sequence[int], drift: float,
+                  heads: Optional[Sequence[int]] = None, gains: Optional[np.ndarray] = None,
+                  threads: int = 0):
+    """Q, K, V of a layer at several denoising steps whose activations drift smoothly.
+
+    Per head, the random parts at step s are cos(s*drift) x_a + sin(s*drift) x_b, where x_a
+    are exactly the parts gen_qkv draws and x_b an independent draw of the same recipe (same
+    frequency scale, its own stream); the stripe term and the gain stay fixed.  Every step has
+    the distribution of the base workload, step 0 is byte-identical to gen_qkv, and two steps
+    d apart have correlation cos(d*drift) in every random part.  Angles |s*drift| are limited
+    to pi/2 (independent draws): past it the rotation turns towards -x_a, and since q.k is
+    unchanged when Q and K both change sign, the masks of step 0 would come back.  Returns one
+    (q, k, v) triple of bf16 bit arrays [1, N, len(heads), D] per entry of `steps`."""
+    steps = list(steps)
+    if any(abs(st * drift) > math.pi / 2 for st in steps):
+        raise ValueError("step * drift must stay within [-pi/2, pi/2]")
+    heads = list(range(cfg.heads)) if heads is None else list(heads)
+    gains = load_gains(cfg) if gains is None else np.asarray(gains, dtype=np.float64)
+    N, D = cfg.N, cfg.head_dim
+    stripe = _stripe_basis(cfg) if cfg.stripes else None
+    out = [[np.empty((1, N, len(heads), D), dtype=np.uint16) for _ in range(3)] for _ in steps]
+
+    def one(slot_head):
+        slot, hd = slot_head
+        rng = _head_rng(cfg, hd)
+        sig = head_sigma(cfg, rng)
+        xa = _components(cfg, rng, sig)
+        rng_b = np.random.Generator(np.random.PCG64(np.random.SeedSequence(
+            cfg.seed, spawn_key=(hd, 1))))
+        head_sigma(cfg, rng_b)                 # same stream layout; the scale is x_a's
+        xb = _components(cfg, rng_b, sig)
+        for si, st in enumerate(steps):
+            th = st * drift
+            if th == 0.0:
+                comps = xa
+            else:
+                c, sn = math.cos(th), math.sin(th)
+                comps = tuple(c * a + sn * b for a, b in zip(xa, xb))
+            qkv = _compose(cfg, comps, float(gains[hd]), stripe)
+            for t in range(3):
+                out[si][t][0, :, slot, :] = bf16_bits_from_f64(qkv[t])
+
+    jobs = list(enumerate(heads))
+    nthr = threads or min(8, os.cpu_count() or 1, len(jobs))
+    if nthr > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(nthr) as ex:
+            list(ex.map(one, jobs))
+    else:
+        for j in jobs:
+            one(j)
+    return [tuple(o) for o in out]
+
