@@ -480,6 +480,11 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
                             pf[2 * tt + hh][e8] = (__bf16)p;
                         }
                 };
+                // From here to the end of O^T += V^T P^T this wavefront wins issue arbitration
+                // over the other wavefront of its SIMD while that one is elsewhere in its loop:
+                // the softmax is the long VALU stretch, and pushing it through keeps the matrix
+                // core fed (measured 2.5-3 % faster, identical results)
+                __builtin_amdgcn_s_setprio(1);
                 // K_{e+1} streams into the K buffer (every wave finished S_e before the last
                 // barrier) while the softmax and PV run
                 constexpr int KPT = Tl::TI / Tl::NKT;    // K DMA instructions per key tile
@@ -514,6 +519,7 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
                     }
                     pin_pipeline<NM, 2>();
                 }
+                __builtin_amdgcn_s_setprio(0);
             }
 
             const float lt = l + other_half(l);

@@ -237,6 +237,9 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnF8Args a) {
                         for (int r = 0; r < 16; ++r) ol[r] *= alpha;
                     m = mn;
                 }
+                // issue priority over the other wavefront of the SIMD from the probabilities to the
+                // end of the PV MFMAs, as in the bf16 kernel (measured 3 % faster, same results)
+                __builtin_amdgcn_s_setprio(1);
                 // probabilities 2^8 exp2(s c - m), cast to E4M3; bytes 16t + e of chunk kc are
                 // element e of key tile 2 kc + t
                 v8i32 pf[2];
@@ -281,6 +284,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnF8Args a) {
                         ol = mfma_f8(ones, pf[1], ol);
                     }
                 }
+                __builtin_amdgcn_s_setprio(0);
             }
 
             // (ExpCast: every row of the all-ones product holds the lane's query's sum)
