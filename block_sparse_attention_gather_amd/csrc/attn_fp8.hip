@@ -52,9 +52,14 @@ typedef int v8i32 __attribute__((ext_vector_type(8)));
 constexpr int kF8Row = 128;                 // bytes per LDS row (D or B fp8 values)
 constexpr int kF8TI = 4;                    // DMA instructions per wave per 16 KiB tile
 
-// 16-byte chunk c of LDS row r is stored at chunk c ^ (r mod 8).
+// 16-byte chunk c of LDS row r is stored at chunk c ^ ((r / 2) mod 8).  The LDS serves the 16
+// lanes of a ds_read_b128 from 256 bytes of banks, i.e. two 128-byte rows: the operand reads
+// take 16 consecutive rows at one chunk, and this swizzle puts them on 16 distinct 16-byte bank
+// groups (row parity picks the half, the XOR the chunk); c ^ (r mod 8) left rows r and r + 8 on
+// the same group (measured: half of all LDS cycles were bank-conflict stalls).
+__device__ __forceinline__ int f8_swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ uint32_t f8_off(int r, int c) {
-    return (uint32_t)(r * kF8Row + ((c ^ (r & 7)) << 4));
+    return (uint32_t)(r * kF8Row + ((c ^ f8_swz(r)) << 4));
 }
 
 // Instruction u (of kF8TI) of wave wv of the DMA of one 16 KiB fp8 tile: 8 rows, lane i
@@ -64,7 +69,7 @@ __device__ __forceinline__ void dma8_part(const uint8_t* sbase, uint32_t lds_add
     const int lr = lane >> 3, pc = lane & 7;
     const int r0 = (wv * kF8TI + u) * 8;
     const int r = r0 + lr;
-    const uint32_t voff = (uint32_t)(lr * kF8Row + ((pc ^ (r & 7)) << 4));
+    const uint32_t voff = (uint32_t)(lr * kF8Row + ((pc ^ f8_swz(r)) << 4));
     const uint8_t* rowbase = sbase + r0 * kF8Row;
     const uint32_t m0 = lds_addr + (uint32_t)((wv * kF8TI + u) * 1024);
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
