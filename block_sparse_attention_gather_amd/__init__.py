@@ -9,6 +9,10 @@ built, or a tensor is not on a GPU, the calls raise.
     row_ptr, col_idx, nnz = score_and_route(q_t, k_t, grid, top_p=0.9, k_floor=8)
     out_t, lse = sparse_attn_fwd(q_t, k_t, v_t, row_ptr, col_idx, grid)
     out = reorder(out_t, grid, inverse=True)      # [b, h, Npad, D] -> [b, N, h, D]
+
+    out, row_ptr, col_idx, nnz = layer(q, k, v, grid, 0.9, 8)   # the same, fused as benchmarked
+    grid_h = grid.with_order(hilbert_order(grid))                # Hilbert-curve token order
+    MaskReuse(2).layer(q, k, v, grid, 0.9, 8)                    # route every 2nd step only
 """
 from __future__ import annotations
 
@@ -547,9 +551,9 @@ def layer(q, k, v, grid: Grid, top_p: float, k_floor: int, scale: Optional[float
 
 
 class MaskReuse:
-    """Mask reuse across denoising steps (DFSAttn page, abstract: sparse masks are cached
-    between steps): the first call of every `interval` consecutive calls routes, the others
-    reuse its CSR.  interval = 1 routes every call.  Host-side bookkeeping only; each call runs
+    """Mask reuse across denoising steps (the DFSAttn page, abstract, caches sparse masks; read
+    here as reuse across the steps of a layer): the first call of every `interval` consecutive
+    calls routes, the others reuse its CSR.  interval = 1 routes every call.  Host-side bookkeeping only; each call runs
     `layer`."""
 
     def __init__(self, interval: int):
