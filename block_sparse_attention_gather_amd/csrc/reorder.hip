@@ -84,8 +84,10 @@ void launch_dir(const uint4* sp, uint4* dp, const GridArgs& ga, dim3 grid, int32
                            sp, dp, ga, heads, dch, N, Npad);
 }
 
-// Forward reorder fused with routing's block pooling: workgroup (j, bh) gathers the B raster
-// rows of block j of (batch, head) bh (head_dim D contiguous elements each) and, each output
+// Forward reorder fused with routing's block pooling: a workgroup gathers the B raster rows of
+// block j of (batch b, head h) (head_dim D contiguous elements each; blockIdx.x = j * heads + h,
+// heads fastest, so the workgroups in flight together read whole raster token rows of all
+// heads rather than one piece of each; blockIdx.y = b) and, each output
 // optional, writes them as the contiguous tiled block (pad rows zero), sums every column over
 // the block's real rows in fp64 (pooled[bh][j] = column sums / real rows; the sums of bf16
 // values are exact in fp64 for the value ranges involved, so the means equal a separate
@@ -99,26 +101,33 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_pool_kernel(
     constexpr int DCH = D / 8;                    // 16-byte chunks per row
     constexpr int RPP = kReorderThreads / DCH;    // rows per pass
     constexpr int NP = B / RPP;                   // passes (rows per thread)
+    static_assert(B <= kReorderThreads, "one thread per block row computes its raster row");
     __shared__ double red[RPP][D + 1];
     __shared__ float amax_red[kReorderThreads / 64];
+    __shared__ uint32_t rows[B];
     const int t = threadIdx.x;
     const int dc = t % DCH, rp = t / DCH;
-    const uint32_t j = blockIdx.x;
-    const uint32_t bh = blockIdx.y;
-    const uint32_t b = bh / (uint32_t)heads, h = bh - b * (uint32_t)heads;
+    const uint32_t n_blk = Npad / B;
+    const uint32_t j = blockIdx.x / (uint32_t)heads, h = blockIdx.x - j * (uint32_t)heads;
+    const uint32_t b = blockIdx.y;
+    const uint32_t bh = b * (uint32_t)heads + h;
     const uint32_t lo = j * B;
     const uint32_t hi = min(lo + (uint32_t)B, N);
+    // The block's raster rows, one per thread of the first B (an explicit order reads its table
+    // here), shared through LDS; then the loads, unconditionally (a row past the last token
+    // reads row 0 and is zeroed afterwards), so that all of them are in flight together.
+    if (t < B) rows[t] = lo + t < N ? tile_pos_to_raster(lo + t, g) : ~0u;
+    __syncthreads();
+    uint32_t n[NP];
+#pragma unroll
+    for (int k = 0; k < NP; ++k) n[k] = rows[rp + RPP * k];
     uint4 v[NP];
 #pragma unroll
-    for (int k = 0; k < NP; ++k) {
-        const uint32_t p = lo + rp + RPP * k;
-        if (p < N) {
-            const uint32_t n = tile_pos_to_raster(p, g);
-            v[k] = src[(((size_t)b * N + n) * heads + h) * DCH + dc];
-        } else {
-            v[k] = make_uint4(0, 0, 0, 0);
-        }
-    }
+    for (int k = 0; k < NP; ++k)
+        v[k] = src[(((size_t)b * N + (n[k] != ~0u ? n[k] : 0u)) * heads + h) * DCH + dc];
+#pragma unroll
+    for (int k = 0; k < NP; ++k)
+        if (n[k] == ~0u) v[k] = make_uint4(0, 0, 0, 0);
     if (dst) {
 #pragma unroll
         for (int k = 0; k < NP; ++k) dst[((size_t)bh * Npad + lo + rp + RPP * k) * DCH + dc] = v[k];
@@ -139,7 +148,7 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_pool_kernel(
         for (int k = 0; k < NP; ++k)
             x8[((size_t)bh * Npad + lo + rp + RPP * k) * DCH + dc] =
                 amax > 0.f ? codes8(v[k], inv) : make_uint2(0, 0);
-        if (t == 0) x8_scales[(size_t)bh * gridDim.x + j] = amax / 448.0f;
+        if (t == 0) x8_scales[(size_t)bh * n_blk + j] = amax / 448.0f;
     }
     if (pooled) {
         double acc[8];
@@ -160,7 +169,7 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_pool_kernel(
         for (int d = t; d < D; d += kReorderThreads) {
             double sum = 0.0;
             for (int r = 0; r < RPP; ++r) sum += red[r][d];
-            pooled[((size_t)bh * gridDim.x + j) * D + d] = sum / (double)(hi - lo);
+            pooled[((size_t)bh * n_blk + j) * D + d] = sum / (double)(hi - lo);
         }
     }
 }
@@ -265,7 +274,10 @@ bsa_status launch_reorder_pool(const void* src, void* dst, double* pooled, void*
                                float* x8_scales, int32_t batch, int32_t heads, int32_t D,
                                const Geometry& g, hipStream_t s) {
     GridArgs ga{g.T, g.H, g.W, g.tt, g.th, g.tw, g.order};
-    const dim3 grid((unsigned)g.n_blk, (unsigned)(batch * heads));
+    if ((uint64_t)g.n_blk * (uint64_t)heads * kReorderThreads > 0xffffffffull)
+        return fail(BSA_ERR_UNSUPPORTED, "reorder_pool: %d blocks x %d heads exceed one grid axis",
+                    g.n_blk, heads);
+    const dim3 grid((unsigned)g.n_blk * (unsigned)heads, (unsigned)batch);
     const uint4* sp = (const uint4*)src;
     uint4* dp = (uint4*)dst;
     uint2* qp = (uint2*)x8;

@@ -107,7 +107,8 @@ BSA_API bsa_status bsa_reorder(const void* src, void* dst, const bsa_shape* shap
  *             bsa_quantize_fp8(v_layout = 0) writes for the tiled tensor (head_dim 128 and
  *             block 128 only, else BSA_ERR_UNSUPPORTED).
  * head_dim 64 or 128, block 64 or 128.  src, dst, x8 16-byte aligned, pooled 8-byte,
- * x8_scales 4-byte aligned; no two buffers may overlap (BSA_ERR_INVALID_ARG). */
+ * x8_scales 4-byte aligned; no two buffers may overlap (BSA_ERR_INVALID_ARG).  n_blk x heads
+ * above 2^24 -> BSA_ERR_UNSUPPORTED. */
 BSA_API bsa_status bsa_reorder_pool(const void* src, void* dst, double* pooled, void* x8,
                                     float* x8_scales, const bsa_shape* shape,
                                     const bsa_grid* grid, void* stream);
@@ -115,7 +116,8 @@ BSA_API bsa_status bsa_reorder_pool(const void* src, void* dst, double* pooled, 
 /* Forward reorder of V fused with its E4M3 quantization (head_dim 128, block 128): v8 and
  * v_scales exactly as bsa_quantize_fp8(v_layout = 1) writes them for the tiled V, and, when dst
  * is not NULL, the tiled bf16 V as bsa_reorder.  Reads the raster V twice (head maxima, then
- * codes).  Alignment and overlap rules as bsa_reorder_pool. */
+ * codes).  Alignment and overlap rules as bsa_reorder_pool; n_blk x heads above 2^24 (a V of
+ * more than 512 GiB) -> BSA_ERR_UNSUPPORTED. */
 BSA_API bsa_status bsa_reorder_quantize_v(const void* src, void* dst, void* v8, float* v_scales,
                                           const bsa_shape* shape, const bsa_grid* grid,
                                           void* stream);
