@@ -95,3 +95,35 @@ def test_fp8_quantization_under_hilbert_order():
     assert np.array_equal(q8.cpu().numpy(), rc) and np.array_equal(qs.cpu().numpy(), rs)
     vc, vsr = F.quantize_v(vt, cfg.block)
     assert np.array_equal(v8.cpu().numpy(), vc) and np.array_equal(vs.cpu().numpy(), vsr)
+
+
+def test_fused_gathers_under_hilbert_order_batch2():
+    """The fused gathers (reorder + block means, E4M3 Q/K codes, V head maxima and codes) take
+    each block's raster rows from the order table once per workgroup and the batch from the
+    grid: batch 2, three heads and a 6-token last block under the Hilbert order, every output
+    bit-identical to the oracle's."""
+    cfgs = [Config("hilb2", 3, 10, 13, 3, 128, 128, (4, 4, 8), 0.9, 2, 131 + 7 * i)
+            for i in range(2)]
+    parts = [gen_qkv(c, gains=np.full(c.heads, 1.5)) for c in cfgs]
+    q = np.concatenate([p[0] for p in parts], axis=0)
+    v = np.concatenate([p[2] for p in parts], axis=0)
+    cfg = cfgs[0]
+    assert cfg.N % cfg.block == 6
+    grid = grid_of(cfg).with_order(bsa.hilbert_order(grid_of(cfg)))
+    pi = O.hilbert_perm(cfg.T, cfg.H, cfg.W)
+    print(f"[gpu] fused gathers under hilbert order batch=2 heads=3 N={cfg.N}", flush=True)
+    tq, tv = to_dev(q), to_dev(v)
+    q_t, qbar = bsa.reorder_pool(tq, grid)
+    _, qbar8, q8, qs = bsa.reorder_pool(tq, grid, tiled=False, fp8=True)
+    v_t, v8, vs = bsa.reorder_quantize_v(tv, grid, tiled=True)
+    torch.cuda.synchronize()
+    qt = O.reorder(q, cfg.T, cfg.H, cfg.W, cfg.tile, cfg.block, pi=pi)
+    vt = O.reorder(v, cfg.T, cfg.H, cfg.W, cfg.tile, cfg.block, pi=pi)
+    assert np.array_equal(to_bits(q_t), qt) and np.array_equal(to_bits(v_t), vt)
+    ref_bar = O.pool(O.widen_bf16(qt), cfg.N, cfg.block)
+    assert np.array_equal(qbar.cpu().numpy(), ref_bar)
+    assert np.array_equal(qbar8.cpu().numpy(), ref_bar)
+    rc, rs = F.quantize_rows(qt, cfg.block)
+    assert np.array_equal(q8.cpu().numpy(), rc) and np.array_equal(qs.cpu().numpy(), rs)
+    vc, vsr = F.quantize_v(vt, cfg.block)
+    assert np.array_equal(v8.cpu().numpy(), vc) and np.array_equal(vs.cpu().numpy(), vsr)
