@@ -34,6 +34,12 @@ CFLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 
+# Per-source compiler options.  attn.hip: LLVM's "max-ilp" machine-scheduling strategy orders
+# the attention loop so that the Wan-480p layer's attention runs 1.2 % faster than under the
+# default strategy (same arithmetic in another instruction order, bitwise-identical outputs;
+# the max-memory-clause and iterative strategies measured slower or equal).
+SOURCE_FLAGS = {"attn.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
 
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -68,11 +74,12 @@ def build(jobs: int = 0, verbose: bool = False, trace: bool = True) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([cc, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *CFLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+                     "-o", obj])
     trace_obj = os.path.join(BUILD, "attn_trace.o")
     if trace:
-        cmds.append([cc, *CFLAGS, "-DBSA_TRACE", "-c", os.path.join(CSRC, "attn.hip"), "-o",
-                     trace_obj])
+        cmds.append([cc, *CFLAGS, *SOURCE_FLAGS.get("attn.hip", []), "-DBSA_TRACE", "-c",
+                     os.path.join(CSRC, "attn.hip"), "-o", trace_obj])
     with ThreadPoolExecutor(jobs or min(len(cmds), os.cpu_count() or 1)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     _link(cc, objs, LIB, verbose)
