@@ -34,11 +34,14 @@ CFLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 
-# Per-source compiler options.  attn.hip: LLVM's "max-ilp" machine-scheduling strategy orders
-# the attention loop so that the Wan-480p layer's attention runs 1.2 % faster than under the
-# default strategy (same arithmetic in another instruction order, bitwise-identical outputs;
-# the max-memory-clause and iterative strategies measured slower or equal).
-SOURCE_FLAGS = {"attn.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# Per-source compiler options: LLVM machine-scheduling strategies that order each attention
+# loop faster than the default on the Wan-480p layer (same arithmetic in another instruction
+# order, bitwise-identical outputs).  attn.hip: "max-ilp", 1.2 % faster (max-memory-clause and
+# the iterative strategies slower or equal).  attn_fp8.hip: "iterative-ilp", 1.3 % faster with
+# the ExpCast cast and 0.9 % with the exact one (max-ilp, max-memory-clause and
+# iterative-minreg slower or equal).
+SOURCE_FLAGS = {"attn.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+                "attn_fp8.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def hipcc() -> str:
