@@ -2,7 +2,8 @@
 
     python -m block_sparse_attention_gather_amd.build [--jobs N] [--verbose] [--no-trace]
 
-Each .hip translation unit is compiled to an object in parallel, then linked into
+Each .hip translation unit is compiled to an object in parallel (the two attention sources
+with a machine-scheduling strategy of their own, SOURCE_FLAGS), then linked into
 block_sparse_attention_gather_amd/libbsa.so.  The same sources with -DBSA_TRACE (per-workgroup
 timestamps of the attention launch, read back with bsa_trace_read) are linked into
 libbsa_trace.so, a debug library for load-balance measurements.  Always recompiles (a build

@@ -49,3 +49,20 @@ def test_traffic_figures_match_the_current_kernel_sources():
         assert got == want
         assert bench.attn_traffic("wan720p", mode) is None       # another workload
     assert bench.attn_traffic("wan480p", "fp8-rne") is None       # never measured
+
+
+def test_kernel_key_covers_per_source_compiler_options():
+    """A per-source compiler option is part of the kernel the traffic figures belong to: the key
+    of a source with options differs from the plain sha256 of the file, and every option set
+    names a source the build compiles."""
+    import hashlib
+    from block_sparse_attention_gather_amd import build as B
+    for src, flags in B.SOURCE_FLAGS.items():
+        assert src in B.SOURCES and flags
+        with open(os.path.join(B.CSRC, src), "rb") as fh:
+            plain = hashlib.sha256(fh.read()).hexdigest()
+        assert bench.src_sha256(src) != plain
+    for src in B.SOURCES:
+        if src not in B.SOURCE_FLAGS:
+            with open(os.path.join(B.CSRC, src), "rb") as fh:
+                assert bench.src_sha256(src) == hashlib.sha256(fh.read()).hexdigest()
