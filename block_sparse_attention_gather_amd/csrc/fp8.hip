@@ -67,9 +67,8 @@ __global__ void zero_kernel(uint32_t* p, int32_t n) {
 // keys 4g..4g+3 of key groups g = t/16 and t/16 + 16, all at 16-byte chunk t mod 16.
 __device__ __forceinline__ int blk_row(int t, int u) { return 4 * ((t >> 4) + 16 * (u >> 2)) + (u & 3); }
 
-// Chunks u = 0..kPer-1 of thread t of block (j, bh): tile-order row j*128 + blk_row(t, u),
-// 16-byte chunk t mod 16 of that row, read from the tiled tensor or gathered from the raster
-// one (zero past the last real token).
+// What a V pass reads: the grid geometry (for the raster gather), heads per batch entry, and
+// the real and padded token counts.
 struct Gather {
     GridArgs g;
     int32_t heads;
@@ -92,8 +91,10 @@ __device__ __forceinline__ Blk blk_of(const Gather& ga) {
     return Blk{(int64_t)j, (int64_t)blockIdx.y * heads + h, blockIdx.y, h};
 }
 
-// rows: kQB words of LDS for the raster rows of the block (written and read here, after a
-// workgroup barrier; RASTER only).
+// Chunks u = 0..kPer-1 of thread t of block (j, bh): tile-order row j*128 + blk_row(t, u),
+// 16-byte chunk t mod 16 of that row, read from the tiled tensor or gathered from the raster
+// one (zero past the last real token).  rows: kQB words of LDS for the block's raster rows
+// (written and read here, around a workgroup barrier; RASTER only).
 template <bool RASTER>
 __device__ __forceinline__ void load_block(uint4 (&c)[kPer], const uint4* __restrict__ x,
                                            const Gather& ga, const Blk& k, int t,
