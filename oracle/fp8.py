@@ -97,45 +97,29 @@ def quantize_rows(xt_bits, B: int):
     return codes, scales
 
 
-def v_key_order(B: int) -> np.ndarray:
-    """Key held at byte position pos of a transposed V row: the order in which one lane of
-    the FP8 kernel holds its probabilities (64-key chunk c, half h, byte b ->
-    key 64c + 32(b // 16) + 8((b % 16) // 4) + 4h + b % 4)."""
-    pos = np.arange(B)
-    c, h, b = pos // 64, (pos % 64) // 32, pos % 32
-    return 64 * c + 32 * (b // 16) + 8 * ((b % 16) // 4) + 4 * h + b % 4
-
-
 def quantize_v(vt_bits, B: int):
-    """Per-(batch, head) E4M3 of tiled bf16 V -> (codes [b, h, n_blk, D, B] u8, each block
-    stored transposed with its keys in v_key_order, scales [b, h] f32)."""
+    """Per-(batch, head) E4M3 of tiled bf16 V [b, h, Npad, D] -> (codes [b, h, Npad, D] u8
+    in the same token-major layout, scales [b, h] f32): one scale set by the largest entry of
+    the whole (batch, head), so the second product needs no per-block rescaling."""
     x = widen_bf16(vt_bits).astype(np.float32)
     b, h, Np, D = x.shape
-    n = Np // B
-    order = v_key_order(B)
-    codes = np.empty((b, h, n, D, B), np.uint8)
+    codes = np.empty(x.shape, np.uint8)
     scales = np.empty((b, h), np.float32)
     for bi in range(b):
         for hi in range(h):
-            c, scales[bi, hi] = _scale_codes(x[bi, hi], np.abs(x[bi, hi]).max())
-            blocks = c.reshape(n, B, D)                          # [block, key, d]
-            codes[bi, hi] = np.transpose(blocks[:, order, :], (0, 2, 1))
+            codes[bi, hi], scales[bi, hi] = _scale_codes(x[bi, hi], np.abs(x[bi, hi]).max())
     return codes, scales
 
 
 def dequantize_rows(codes, scales, B: int) -> np.ndarray:
+    """Per-block codes [b, h, Npad, D] and scales [b, h, n_blk] -> fp64 [b, h, Npad, D]."""
     v = e4m3_decode(codes)
     return v * np.repeat(scales.astype(np.float64), B, axis=2)[..., None]
 
 
-def dequantize_v(codes, scales, B: int) -> np.ndarray:
-    """Block-transposed V codes -> tiled [b, h, Npad, D] fp64."""
-    b, h, n, D, _ = codes.shape
-    order = v_key_order(B)
-    v = e4m3_decode(codes)                                       # [b, h, n, D, B]
-    out = np.empty((b, h, n, B, D))
-    out[:, :, :, order, :] = np.transpose(v, (0, 1, 2, 4, 3))
-    return out.reshape(b, h, n * B, D) * scales.astype(np.float64)[:, :, None, None]
+def dequantize_v(codes, scales) -> np.ndarray:
+    """Per-head codes [b, h, Npad, D] and scales [b, h] -> fp64 [b, h, Npad, D]."""
+    return e4m3_decode(codes) * scales.astype(np.float64)[:, :, None, None]
 
 
 def attn_error_bound(q, k, v, row_ptr, col_idx, N: int, B: int, scale: float, rows):
@@ -160,6 +144,26 @@ def attn_error_bound(q, k, v, row_ptr, col_idx, N: int, B: int, scale: float, ro
         w /= w.sum(axis=1, keepdims=True)
         av = np.abs(v[bi, hi, keys])
         out[(bi, hi, i)] = 2.0 ** -4 * (w @ av) + 2.0 ** -18 * av.sum(axis=0)[None, :]
+    return out
+
+
+def abs_weighted_v(q, k, v, row_ptr, col_idx, N: int, B: int, scale: float, rows):
+    """sum_u w_u |v_u| per element for the listed rows (b, h, i): the exact softmax weights
+    w of the row's real keys over fp64 q, k, v [b, h, Npad, D], applied to |v|.  It is the
+    size against which rounding in the kernel's fp32 arithmetic is measured (a relative error
+    r in every weight moves the output by at most r times this).  Returns
+    {row: [rows of the block, D]}."""
+    n = num_blocks(N, B)
+    out = {}
+    for (bi, hi, i) in rows:
+        r = (bi * q.shape[1] + hi) * n + i
+        sel = col_idx[row_ptr[r]:row_ptr[r + 1]]
+        keys = np.concatenate([np.arange(j * B, min((j + 1) * B, N)) for j in sel])
+        lo, hi_ = i * B, min((i + 1) * B, N)
+        lg = scale * (q[bi, hi, lo:hi_] @ k[bi, hi, keys].T)
+        w = np.exp(lg - lg.max(axis=1, keepdims=True))
+        w /= w.sum(axis=1, keepdims=True)
+        out[(bi, hi, i)] = w @ np.abs(v[bi, hi, keys])
     return out
 
 

@@ -65,24 +65,48 @@ def test_quantize_rows_scale_and_error():
                 assert np.all(err <= 2.0 ** -4 * np.abs(blk) * 1.0001 + 2.0 ** -10 * s[bi, hi, j])
 
 
-def test_v_layout_roundtrip():
+def test_quantize_v_one_scale_per_head():
+    """V takes one scale per (batch, head): the same codes and scale as quantizing the whole
+    head as one block; dequantized within half an E4M3 ulp; a head of zeros gets scale 0."""
     rng = np.random.default_rng(2)
     B, D = 128, 64
-    order = fp8.v_key_order(B)
-    assert sorted(order.tolist()) == list(range(B))
-    # the first 16 positions of half 0 are the keys one lane holds of the first 32-key tile
-    assert order[:16].tolist() == [8 * g + u for g in range(4) for u in range(4)]
-    assert order[32:48].tolist() == [8 * g + 4 + u for g in range(4) for u in range(4)]
-    x = rng.standard_normal((1, 2, 2 * B, D))
+    x = rng.standard_normal((2, 3, 2 * B, D)) * np.array([0.02, 1.0, 40.0])[None, :, None, None]
+    x[1, 0] = 0.0
     bits = _bf16_bits(x)
     codes, s = fp8.quantize_v(bits, B)
-    assert codes.shape == (1, 2, 2, D, B)
-    # block 1, feature 3, position p holds key order[p] of block 1
-    c_rows, _ = fp8.quantize_rows(bits, 2 * B)                   # same per-head scale
-    assert np.array_equal(codes[0, 1, 1, 3], c_rows[0, 1, B + order, 3])
-    deq = fp8.dequantize_v(codes, s, B)
+    assert codes.shape == (2, 3, 2 * B, D) and s.shape == (2, 3)
+    c_one, s_one = fp8.quantize_rows(bits, 2 * B)                # one block = the whole head
+    assert np.array_equal(codes, c_one) and np.array_equal(s, s_one[:, :, 0])
+    assert s[1, 0] == 0 and not codes[1, 0].any()
     xv = fp8.widen_bf16(bits)
-    assert np.all(np.abs(deq - xv) <= 2.0 ** -4 * np.abs(xv) * 1.0001 + 2.0 ** -10 * s[:, :, None, None])
+    for bi in range(2):
+        for hi in range(3):
+            if s[bi, hi] == 0:
+                continue
+            assert np.abs(fp8.e4m3_decode(codes[bi, hi])).max() == 448.0
+    deq = fp8.dequantize_v(codes, s)
+    assert np.all(np.abs(deq - xv) <= 2.0 ** -4 * np.abs(xv) * 1.0001
+                  + 2.0 ** -10 * s[:, :, None, None])
+
+
+def test_v8_layout_helper_is_a_bijection():
+    """The test-side map between the library's block-transposed V codes and the token-major
+    codes of the oracle: inverse of each other, and the first positions of a row hold the keys
+    the header lists for them."""
+    from fp8_support import tokens_to_v8, v8_key_order, v8_to_tokens
+    B, D = 128, 128
+    order = v8_key_order(B)
+    assert sorted(order.tolist()) == list(range(B))
+    # bytes 0..15 of half 0: keys 0-3, 8-11, 16-19, 24-27; bytes 32..47 (half 1): +4
+    assert order[:16].tolist() == [8 * g + u for g in range(4) for u in range(4)]
+    assert order[32:48].tolist() == [8 * g + 4 + u for g in range(4) for u in range(4)]
+    assert order[64:80].tolist() == [64 + 8 * g + u for g in range(4) for u in range(4)]
+    rng = np.random.default_rng(5)
+    tok = rng.integers(0, 255, size=(1, 2, 3 * B, D), dtype=np.uint8)
+    v8 = tokens_to_v8(tok, B)
+    assert v8.shape == (1, 2, 3, D, B)
+    assert v8[0, 1, 2, 5, 7] == tok[0, 1, 2 * B + order[7], 5]
+    assert np.array_equal(v8_to_tokens(v8), tok)
 
 
 def test_error_bound_holds_for_simulated_cast():
