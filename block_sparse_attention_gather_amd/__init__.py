@@ -192,6 +192,14 @@ def _require(t, dtype, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _need(t, dtype, shape, name):
+    """t must be a contiguous GPU tensor of `dtype` with exactly `shape`: the C ABI sees only
+    a pointer, so a smaller buffer would be written out of bounds."""
+    _require(t, dtype, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def _shape(batch, heads, D) -> _Shape:
     return _Shape(batch, heads, D)
 
@@ -255,8 +263,8 @@ def reorder_pool(x, grid: Grid, out=None, pooled=None, tiled: bool = True, fp8: 
             x8 = torch.empty((b, h, grid.Npad, D), dtype=torch.uint8, device=dev)
         if x8_scales is None:
             x8_scales = torch.empty((b, h, grid.n_blk), dtype=torch.float32, device=dev)
-        _require(x8, torch.uint8, "x8")
-        _require(x8_scales, torch.float32, "x8_scales")
+        _need(x8, torch.uint8, (b, h, grid.Npad, D), "x8")
+        _need(x8_scales, torch.float32, (b, h, grid.n_blk), "x8_scales")
     g, s = grid._c(), _shape(b, h, D)
     _check(_load().bsa_reorder_pool(x.data_ptr(), _ptr(out), _ptr(pooled),
                                     _ptr(x8) if fp8 else None,
@@ -278,12 +286,14 @@ def reorder_quantize_v(x, grid: Grid, out=None, tiled: bool = False, v8=None, v_
     dev = x.device
     if tiled and out is None:
         out = torch.empty((b, h, grid.Npad, D), dtype=x.dtype, device=dev)
+    if out is not None:
+        _need(out, torch.bfloat16, (b, h, grid.Npad, D), "out")
     if v8 is None:
         v8 = torch.empty((b, h, grid.n_blk, D, grid.block), dtype=torch.uint8, device=dev)
     if v_scales is None:
         v_scales = torch.empty((b, h), dtype=torch.float32, device=dev)
-    _require(v8, torch.uint8, "v8")
-    _require(v_scales, torch.float32, "v_scales")
+    _need(v8, torch.uint8, (b, h, grid.n_blk, D, grid.block), "v8")
+    _need(v_scales, torch.float32, (b, h), "v_scales")
     g, s = grid._c(), _shape(b, h, D)
     _check(_load().bsa_reorder_quantize_v(x.data_ptr(), _ptr(out), v8.data_ptr(),
                                           v_scales.data_ptr(), ctypes.byref(s), ctypes.byref(g),
@@ -441,13 +451,17 @@ def sparse_attn_fwd(q_t, k_t, v_t, row_ptr, col_idx, grid: Grid,
         raise ValueError(f"tiled tensors need {grid.Npad} rows")
     if row_ptr.numel() != b * h * grid.n_blk + 1:
         raise ValueError("row_ptr must have rows + 1 entries")
+    if col_idx.dim() != 1 or col_idx.numel() < 1:
+        raise ValueError("col_idx must be a 1-D tensor holding at least row_ptr[rows] entries")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     dev = q_t.device
     if out is None:
         out = torch.empty_like(q_t)
-    _require(out, torch.bfloat16, "out")
+    _need(out, torch.bfloat16, (b, h, Np, D), "out")
     if return_lse and lse is None:
         lse = torch.empty((b, h, Np), dtype=torch.float32, device=dev)
+    if return_lse:
+        _need(lse, torch.float32, (b, h, Np), "lse")
     if workspace is None:
         workspace = torch.empty(attn_workspace_bytes(b, h, D, grid), dtype=torch.uint8,
                                 device=dev)
@@ -505,13 +519,22 @@ def sparse_attn_fwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, row_ptr, col_idx,
         raise ValueError("k8 must match q8, v8 must be [b, h, n_blk, D, B]")
     if row_ptr.numel() != b * h * grid.n_blk + 1:
         raise ValueError("row_ptr must have rows + 1 entries")
+    if col_idx.dim() != 1 or col_idx.numel() < 1:
+        raise ValueError("col_idx must be a 1-D tensor holding at least row_ptr[rows] entries")
+    if Np != grid.Npad:
+        raise ValueError(f"q8/k8 need {grid.Npad} rows")
+    _need(q_scale, torch.float32, (b, h, grid.n_blk), "q_scale")
+    _need(k_scale, torch.float32, (b, h, grid.n_blk), "k_scale")
+    _need(v_scale, torch.float32, (b, h), "v_scale")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     dev = q8.device
     if out is None:
         out = torch.empty((b, h, Np, D), dtype=torch.bfloat16, device=dev)
-    _require(out, torch.bfloat16, "out")
+    _need(out, torch.bfloat16, (b, h, Np, D), "out")
     if return_lse and lse is None:
         lse = torch.empty((b, h, Np), dtype=torch.float32, device=dev)
+    if return_lse:
+        _need(lse, torch.float32, (b, h, Np), "lse")
     g, s = grid._c(), _shape(b, h, D)
     if workspace is None:
         n = int(_load().bsa_attn_fp8_workspace_bytes(ctypes.byref(s), ctypes.byref(g)))

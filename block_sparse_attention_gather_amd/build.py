@@ -52,10 +52,34 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libbsa)")
 
 
+_FEATURE_PROBE = """#include <hip/hip_runtime.h>
+__global__ void bsa_feature_probe(float* x) { x[threadIdx.x] *= 2.0f; }
+"""
+
+
+def check_device_flags(cc: str) -> None:
+    """Compile a one-line kernel for the device only with CFLAGS: the host pass of a full
+    compile always warns that it does not know the packed-fp32 feature (harmless, and filtered
+    from the build log below), but the device pass must accept it, or the flag that keeps
+    packed fp32 instructions out of the code would silently do nothing."""
+    os.makedirs(BUILD, exist_ok=True)
+    src = os.path.join(BUILD, "feature_probe.hip")
+    with open(src, "w") as fh:
+        fh.write(_FEATURE_PROBE)
+    cmd = [cc, *CFLAGS, "--offload-device-only", "-c", src,
+           "-o", os.path.join(BUILD, "feature_probe.o")]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0 or "not a recognized feature" in r.stdout:
+        raise RuntimeError("the device compiler does not accept the build's target features:\n"
+                           + r.stdout)
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # the host pass of every compile warns about the device-only feature (check_device_flags
+    # proves that the device pass accepts it)
     out = "\n".join(l for l in r.stdout.splitlines()
                     if "packed-fp32-ops" not in l and "not a recognized feature" not in l)
     if r.returncode != 0:
@@ -73,6 +97,7 @@ def _link(cc, objs, lib, verbose):
 def build(jobs: int = 0, verbose: bool = False, trace: bool = True) -> str:
     cc = hipcc()
     os.makedirs(BUILD, exist_ok=True)
+    check_device_flags(cc)
     objs = []
     cmds = []
     for src in SOURCES:

@@ -1,5 +1,6 @@
-"""bench.py's host logic (CPU only, no GPU touched): the one-GPU guard, argument checks, and
-the recorded HBM traffic figures, which belong to exactly one attention source and mode."""
+"""bench.py's host logic (CPU only, no GPU touched): the one-GPU guard, argument checks, the
+recorded HBM traffic figures (each belongs to exactly one attention source, mode and workload)
+and the host description of the CPU baseline."""
 import json
 import os
 import subprocess
@@ -38,17 +39,31 @@ def test_parse_tile():
     assert bench.parse_tile("8,4,4") == (8, 4, 4)
 
 
-def test_traffic_figures_match_the_current_kernel_sources():
-    """The recorded FETCH/WRITE figures are reported only for the attention source and mode
-    they were measured on; both figures in the table belong to the sources as they are now."""
-    for mode, t in bench.ATTN_TRAFFIC.items():
-        assert bench.src_sha256(t["src"]) == t["sha256"], (mode, "re-take the counters")
-        got = bench.attn_traffic(t["config"], mode)
-        want = int(round((t["fetch_kib"] * bench.FETCH_SCALE
-                          + t["write_kib"] * bench.WRITE_SCALE) * 1024))
-        assert got == want
-        assert bench.attn_traffic("wan720p", mode) is None       # another workload
-    assert bench.attn_traffic("wan480p", "fp8-rne") is None       # never measured
+def test_traffic_figures_belong_to_one_kernel_mode_and_workload():
+    """A recorded FETCH/WRITE figure is reported only for the attention source (and its
+    compiler options), mode and workload it was measured on; any other source gives null."""
+    keys = set()
+    for t in bench.ATTN_TRAFFIC:
+        key = (t["mode"], t["config"])
+        assert key not in keys
+        keys.add(key)
+        got = bench.attn_traffic(t["config"], t["mode"])
+        if bench.src_sha256(t["src"]) == t["sha256"]:
+            want = int(round((t["fetch_kib"] * bench.FETCH_SCALE
+                              + t["write_kib"] * bench.WRITE_SCALE) * 1024))
+            assert got == want
+        else:
+            assert got is None                                  # taken on another kernel
+    assert bench.attn_traffic("small", "bf16") is None            # never measured
+    assert bench.attn_traffic("wan480p", "fp8-rne") is None
+
+
+def test_traffic_lookup_rejects_a_changed_source(monkeypatch):
+    t = dict(bench.ATTN_TRAFFIC[0])
+    monkeypatch.setattr(bench, "ATTN_TRAFFIC", [dict(t, sha256=bench.src_sha256(t["src"])),
+                                                dict(t, config="tiny", sha256="0" * 64)])
+    assert bench.attn_traffic(t["config"], t["mode"]) is not None
+    assert bench.attn_traffic("tiny", t["mode"]) is None
 
 
 def test_kernel_key_covers_per_source_compiler_options():
@@ -66,3 +81,23 @@ def test_kernel_key_covers_per_source_compiler_options():
         if src not in B.SOURCE_FLAGS:
             with open(os.path.join(B.CSRC, src), "rb") as fh:
                 assert bench.src_sha256(src) == hashlib.sha256(fh.read()).hexdigest()
+
+
+def test_host_info_describes_the_cpu():
+    h = bench.host_info()
+    assert h["os_cpu_count"] == os.cpu_count()
+    assert 1 <= h["affinity_cpus"] <= os.cpu_count()
+    assert h["physical_cores"] is None or 1 <= h["physical_cores"] <= os.cpu_count()
+    assert isinstance(h["blas"], list)
+
+
+def test_default_workload_is_the_largest_video_layer():
+    import argparse
+    old = sys.argv
+    try:
+        sys.argv = ["bench.py"]
+        a = bench.parse()
+    finally:
+        sys.argv = old
+    assert isinstance(a, argparse.Namespace)
+    assert a.config == "hunyuan720p" and a.gpus == 1 and a.cpu_stride == 0
