@@ -114,6 +114,7 @@ def _load():
         "bsa_sparse_attn_fwd_fp8": (I32, [P, P, P, P, P, P, P, P, S, G, F32, I32, P, P, P, SZ,
                                            P]),
         "bsa_sparse_attn_fwd": (I32, [P, P, P, P, P, S, G, F32, P, P, P, SZ, P]),
+        "bsa_sparse_attn_fwd_noalloc": (I32, [P, P, P, P, P, S, G, F32, P, P, P]),
         "bsa_last_error": (ctypes.c_char_p, []),
         "bsa_version": (ctypes.c_char_p, []),
     }
@@ -472,6 +473,37 @@ def sparse_attn_fwd(q_t, k_t, v_t, row_ptr, col_idx, grid: Grid,
         _ptr(lse) if return_lse else None, workspace.data_ptr(), workspace.numel(),
         _stream(q_t)))
     return out, (lse if return_lse else None)
+
+
+def sparse_attn_fwd_noalloc(q_t, k_t, v_t, row_ptr, col_idx, grid: Grid, out, lse=None,
+                            scale: Optional[float] = None):
+    """sparse_attn_fwd for callers that cannot allocate: the caller passes the output (and
+    optionally lse) buffers, and the library works in its static per-device scratch instead
+    of a workspace.  Same result as sparse_attn_fwd, bit for bit.  Calls that overlap on one
+    device share that scratch and must be ordered.  Returns (out, lse)."""
+    import torch
+    for t, n in ((q_t, "q_t"), (k_t, "k_t"), (v_t, "v_t")):
+        _require(t, torch.bfloat16, n)
+    _require(row_ptr, torch.int32, "row_ptr")
+    _require(col_idx, torch.int32, "col_idx")
+    b, h, Np, D = q_t.shape
+    if tuple(k_t.shape) != (b, h, Np, D) or tuple(v_t.shape) != (b, h, Np, D):
+        raise ValueError("q_t/k_t/v_t must have the same shape")
+    if Np != grid.Npad:
+        raise ValueError(f"tiled tensors need {grid.Npad} rows")
+    if row_ptr.numel() != b * h * grid.n_blk + 1:
+        raise ValueError("row_ptr must have rows + 1 entries")
+    if col_idx.dim() != 1 or col_idx.numel() < 1:
+        raise ValueError("col_idx must be a 1-D tensor holding at least row_ptr[rows] entries")
+    _need(out, torch.bfloat16, (b, h, Np, D), "out")
+    if lse is not None:
+        _need(lse, torch.float32, (b, h, Np), "lse")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    g, s = grid._c(), _shape(b, h, D)
+    _check(_load().bsa_sparse_attn_fwd_noalloc(
+        q_t.data_ptr(), k_t.data_ptr(), v_t.data_ptr(), row_ptr.data_ptr(), col_idx.data_ptr(),
+        ctypes.byref(s), ctypes.byref(g), scale, out.data_ptr(), _ptr(lse), _stream(q_t)))
+    return out, lse
 
 
 def quantize_fp8(x_t, grid: Grid, v_layout: bool = False, out=None, scales=None):

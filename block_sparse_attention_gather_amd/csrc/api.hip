@@ -420,6 +420,36 @@ bsa_status bsa_sparse_attn_fwd(const void* q_t, const void* k_t, const void* v_t
                        shape->head_dim, g, scale, out_t, lse, ws, dev, (hipStream_t)stream);
 }
 
+bsa_status bsa_sparse_attn_fwd_noalloc(const void* q_t, const void* k_t, const void* v_t,
+                                       const int32_t* row_ptr, const int32_t* col_idx,
+                                       const bsa_shape* shape, const bsa_grid* grid,
+                                       float scale, void* out_t, float* lse, void* stream) {
+    Geometry g;
+    bsa_status st = geometry(grid, &g);
+    if (st != BSA_OK) return st;
+    if ((st = check_shape(shape)) != BSA_OK) return st;
+    if (!q_t || !k_t || !v_t || !row_ptr || !col_idx || !out_t)
+        return fail(BSA_ERR_INVALID_ARG, "q_t, k_t, v_t, row_ptr, col_idx, out_t must be non-NULL");
+    if (!(scale > 0.f) || !isfinite(scale))
+        return fail(BSA_ERR_INVALID_ARG, "scale must be finite and positive");
+    if ((st = check_kernel_dims(shape, g)) != BSA_OK) return st;
+    if ((((uintptr_t)q_t | (uintptr_t)k_t | (uintptr_t)v_t | (uintptr_t)out_t) & 15))
+        return fail(BSA_ERR_INVALID_ARG, "q_t/k_t/v_t/out_t must be 16-byte aligned");
+    DeviceInfo dev;
+    if ((st = device_info(&dev)) != BSA_OK) return st;
+    const size_t need = attn_ws_bytes(shape->batch, shape->heads, shape->head_dim, g,
+                                      attn_slots(shape->head_dim, g.B, dev));
+    if (need > kStaticScratchBytes)
+        return fail(BSA_ERR_WORKSPACE,
+                    "this call needs %zu bytes of attention workspace, more than the %zu-byte "
+                    "static scratch of bsa_sparse_attn_fwd_noalloc (use bsa_sparse_attn_fwd)",
+                    need, kStaticScratchBytes);
+    void* ws = nullptr;
+    if ((st = static_scratch(dev.device, &ws)) != BSA_OK) return st;
+    return launch_attn(q_t, k_t, v_t, row_ptr, col_idx, shape->batch, shape->heads,
+                       shape->head_dim, g, scale, out_t, lse, ws, dev, (hipStream_t)stream);
+}
+
 const char* bsa_last_error(void) { return g_err; }
 
 const char* bsa_version(void) { return BSA_VERSION_STRING; }

@@ -29,6 +29,8 @@
 // (ds_read_b64_tr_b16), and the 16-byte chunks of each tile row are XOR-swizzled by the row
 // index (K: c ^ (r mod C), V: c ^ (4r mod C), C = D/8 chunks a row) so neither read pattern
 // has bank conflicts.
+#include <mutex>
+
 #include "attn_common.h"
 
 namespace bsa {
@@ -685,6 +687,35 @@ bsa_status launch_plan(const int32_t* row_ptr, int32_t batch, int32_t heads, int
     hipLaunchKernelGGL(plan_rows_kernel, dim3(nbh), dim3(kPlanThreads), 0, s, row_ptr, g.n_blk,
                        hdr, head_item_off, head_slot_base, items, done);
     return check_launch("plan_rows");
+}
+
+// ---------------------------------------------------------------------------------------
+// static scratch of bsa_sparse_attn_fwd_noalloc
+// ---------------------------------------------------------------------------------------
+// The attention workspace (schedule header, work items, split-row counters and fp32
+// partials) for callers that cannot allocate: one array per device, alive until the process
+// ends.  Host code never passes `scratch` itself to a kernel (in host code the name is only a
+// stand-in for the device symbol); it passes the device address that hipGetSymbolAddress
+// returns for the current device, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+bsa_status static_scratch(int device, void** ptr) {
+    if (device < 0 || device >= kMaxDevices)
+        return fail(BSA_ERR_HIP, "device ordinal %d out of range", device);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(BSA_ERR_HIP, "static scratch of device %d: hipGetSymbolAddress: %s",
+                        device, hipGetErrorString(e));
+        g_scratch_ptr[device] = p;
+    }
+    *ptr = g_scratch_ptr[device];
+    return BSA_OK;
 }
 
 int attn_max_heads() { return kMaxHeads; }

@@ -121,6 +121,12 @@ bsa_status launch_scan(const int32_t* counts, int32_t* excl, int32_t* total, int
                        hipStream_t s);
 
 size_t attn_ws_bytes(int32_t batch, int32_t heads, int32_t D, const Geometry& g, int slots);
+// Static scratch of bsa_sparse_attn_fwd_noalloc: kStaticScratchBytes of device memory per
+// device (a file-scope __device__ array), its address on `device` (the current device) looked
+// up once with hipGetSymbolAddress and cached.
+constexpr size_t kStaticScratchBytes = (size_t)136 << 20;
+constexpr int kMaxDevices = 64;
+bsa_status static_scratch(int device, void** ptr);
 bsa_status launch_attn(const void* q_t, const void* k_t, const void* v_t,
                        const int32_t* row_ptr, const int32_t* col_idx, int32_t batch,
                        int32_t heads, int32_t D, const Geometry& g, float scale, void* out_t,

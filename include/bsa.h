@@ -228,6 +228,24 @@ BSA_API bsa_status bsa_sparse_attn_fwd(const void* q_t, const void* k_t, const v
                                void* out_t, float* lse, void* ws, size_t ws_bytes,
                                void* stream);
 
+/* bsa_sparse_attn_fwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same computation, the
+ * same arguments without ws / ws_bytes, and the same output bit for bit.  Instead of a caller's
+ * workspace it uses a static scratch array of 136 MiB per device (allocated when the library's
+ * device code is loaded onto that device, held until the process ends; its address is looked
+ * up once per device on the first call made with that device current).  The call itself
+ * allocates nothing.  The schedule kernels rewrite every scratch word the attention reads, so
+ * no state carries over from an earlier call.  Calls that overlap on one device (on different
+ * streams, or from several threads without ordering) share the one array and race: order them.
+ * A call whose workspace (bsa_attn_workspace_bytes) exceeds 136 MiB -> BSA_ERR_WORKSPACE
+ * (on a 256-CU MI355X that is more than about 390,000 rows batch*heads*n_blk at block 128);
+ * every other error as bsa_sparse_attn_fwd. */
+BSA_API bsa_status bsa_sparse_attn_fwd_noalloc(const void* q_t, const void* k_t,
+                                               const void* v_t, const int32_t* row_ptr,
+                                               const int32_t* col_idx, const bsa_shape* shape,
+                                               const bsa_grid* grid, float scale, void* out_t,
+                                               float* lse, void* stream);
+
 /* ---- 4. FP8 (E4M3) attention (VC-Attention page, abstract) ------------------------- */
 /* Both products on FP8 matrix cores with fp32 accumulation; head_dim 128 and block 128 only
  * (other shapes -> BSA_ERR_UNSUPPORTED).  E4M3 is the OCP 8-bit format (4 exponent bits,

@@ -31,7 +31,7 @@ def test_header_compiles_as_c99_and_cxx(tmp_path):
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     lib = ctypes.CDLL(bsa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -226,6 +226,24 @@ def test_attn_validation_before_device_query():
     st = L.bsa_sparse_attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s), ctypes.byref(g),
                                float("nan"), FAKE, None, FAKE, 1 << 30, None)
     assert st == -1
+
+
+def test_noalloc_attn_validation_before_device_query():
+    """bsa_sparse_attn_fwd_noalloc checks its arguments like bsa_sparse_attn_fwd before it
+    looks at the device or its static scratch."""
+    L = bsa.lib()
+    g = bsa.Grid(2, 16, 16, (4, 4, 4), 64)._c()
+    s = bsa._Shape(1, 2, 64)
+    st = L.bsa_sparse_attn_fwd_noalloc(FAKE, FAKE, None, FAKE, FAKE, ctypes.byref(s),
+                                       ctypes.byref(g), 0.125, FAKE, None, None)
+    assert st == -1 and b"non-NULL" in L.bsa_last_error()
+    s96 = bsa._Shape(1, 2, 96)
+    assert L.bsa_sparse_attn_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s96),
+                                         ctypes.byref(g), 0.125, FAKE, None, None) == -2
+    assert L.bsa_sparse_attn_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s),
+                                         ctypes.byref(g), -1.0, FAKE, None, None) == -1
+    assert L.bsa_sparse_attn_fwd_noalloc(FAKE + 8, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s),
+                                         ctypes.byref(g), 0.125, FAKE, None, None) == -1
 
 
 def test_route_workspace_size_is_host_computable():
