@@ -39,76 +39,88 @@ namespace {
 // ---------------------------------------------------------------------------------------
 // planner
 // ---------------------------------------------------------------------------------------
+// Head mode (plan.h).  One workgroup: Kc; per head its kept blocks, work items and partial
+// slots (a wavefront per head); heads ranked by cost (bitonic sort of plan::head_key in LDS)
+// and given longest-first to the least-loaded XCD queue; queue starts and lengths; every head's
+// first item (head_off) and first partial slot; queue counters reset.
 __global__ __launch_bounds__(kPlanThreads) void plan_global_kernel(
     const int32_t* __restrict__ row_ptr, int32_t n_blk, int32_t nbh, int32_t target,
-    int32_t* __restrict__ hdr, int32_t* __restrict__ head_item_off,
+    int32_t* __restrict__ hdr, int32_t* __restrict__ head_off,
     int32_t* __restrict__ head_slot_base) {
-    __shared__ int32_t hitems[kMaxHeads], hslots[kMaxHeads], hcost[kMaxHeads];
-    __shared__ int32_t horder[kMaxHeads], hqueue[kMaxHeads];
-    __shared__ int64_t qload[kNQ];
-    __shared__ int32_t qlen[kNQ], qstart[kNQ], qrun[kNQ];
+    __shared__ int32_t hitems[kMaxHeads], hslots[kMaxHeads], horder[kMaxHeads];
+    __shared__ uint64_t hkey[kMaxHeads];
+    __shared__ int64_t hcost[kMaxHeads];
     const int t = threadIdx.x;
     const int64_t rows = (int64_t)nbh * n_blk;
-    const int64_t total = row_ptr[rows];
-    int64_t kc64 = (total + target - 1) / target;
-    const int32_t Kc = (int32_t)(kc64 < kKcMin ? kKcMin : kc64);
-    for (int h = t; h < nbh; h += kPlanThreads)
-        hcost[h] = row_ptr[(int64_t)(h + 1) * n_blk] - row_ptr[(int64_t)h * n_blk];
-    // work items and partial slots per head: one wavefront sums one head's rows
+    const int32_t Kc = plan::chunk_size(row_ptr[rows], target);
     {
         const int lane = t & 63, w = t >> 6;
         for (int h = w; h < nbh; h += kPlanThreads / 64) {
-            int32_t ni_sum = 0, ns_sum = 0;
-#pragma unroll 8
+            int32_t ni = 0, ns = 0;
+            int64_t hc = 0;
             for (int i = lane; i < n_blk; i += 64) {
                 const int64_t r = (int64_t)h * n_blk + i;
                 const int32_t c = row_ptr[r + 1] - row_ptr[r];
-                int32_t ni = (c + Kc - 1) / Kc;
-                ni = ni < 1 ? 1 : ni;
-                ni_sum += ni;
-                ns_sum += ni > 1 ? ni : 0;
+                ni += plan::row_items(c, Kc);
+                ns += plan::row_slots(c, Kc);
+                hc += c;
             }
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) {
-                ni_sum += __shfl_xor(ni_sum, off, 64);
-                ns_sum += __shfl_xor(ns_sum, off, 64);
+                ni += __shfl_xor(ni, off, 64);
+                ns += __shfl_xor(ns, off, 64);
+                hc += __shfl_xor(hc, off, 64);
             }
             if (lane == 0) {
-                hitems[h] = ni_sum;
-                hslots[h] = ns_sum;
+                hitems[h] = ni;
+                hslots[h] = ns;
+                hcost[h] = hc;
+                hkey[h] = plan::head_key(hc, h);
             }
         }
     }
+    // heads ranked by cost descending (ties by index): bitonic sort of the head keys
+    int P2 = 1;
+    while (P2 < nbh) P2 <<= 1;
+    for (int h = nbh + t; h < P2; h += kPlanThreads) hkey[h] = ~(uint64_t)0;
     __syncthreads();
-    // heads ranked by cost (kept blocks) descending, ties by index
-    for (int h = t; h < nbh; h += kPlanThreads) {
-        const int32_t ch = hcost[h];
-        int rk = 0;
-        for (int h2 = 0; h2 < nbh; ++h2) {
-            const int32_t c2 = hcost[h2];
-            rk += (c2 > ch) || (c2 == ch && h2 < h);
+    for (int kk = 2; kk <= P2; kk <<= 1)
+        for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+            for (int i = t; i < P2; i += kPlanThreads) {
+                const int l = i ^ jj;
+                if (l > i) {
+                    const uint64_t x = hkey[i], y = hkey[l];
+                    if ((x > y) == ((i & kk) == 0)) {
+                        hkey[i] = y;
+                        hkey[l] = x;
+                    }
+                }
+            }
+            __syncthreads();
         }
-        horder[rk] = h;
-    }
+    for (int r = t; r < nbh; r += kPlanThreads) horder[r] = plan::key_head(hkey[r]);
     __syncthreads();
     if (t == 0) {
+        // longest processing time first: each head to the least-loaded queue (ties: lowest);
+        // head_off temporarily holds the head's queue
+        int64_t qload[kNQ];
+        int32_t qlen[kNQ], qstart[kNQ], qrun[kNQ];
         for (int q = 0; q < kNQ; ++q) { qload[q] = 0; qlen[q] = 0; qrun[q] = 0; }
-        // longest-processing-time-first: each head to the least-loaded queue
-        for (int k = 0; k < nbh; ++k) {
-            const int h = horder[k];
+        for (int r = 0; r < nbh; ++r) {
+            const int h = horder[r];
             int best = 0;
             for (int q = 1; q < kNQ; ++q)
                 if (qload[q] < qload[best]) best = q;
             qload[best] += hcost[h];
             qlen[best] += hitems[h];
-            hqueue[h] = best;
+            head_off[h] = best;
         }
         int32_t acc = 0;
         for (int q = 0; q < kNQ; ++q) { qstart[q] = acc; acc += qlen[q]; }
-        for (int k = 0; k < nbh; ++k) {
-            const int h = horder[k];
-            const int q = hqueue[h];
-            head_item_off[h] = qstart[q] + qrun[q];
+        for (int r = 0; r < nbh; ++r) {
+            const int h = horder[r];
+            const int q = head_off[h];
+            head_off[h] = qstart[q] + qrun[q];
             qrun[q] += hitems[h];
         }
         int32_t sacc = 0;
@@ -122,9 +134,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_global_kernel(
     }
 }
 
+// Head mode.  One workgroup per head: rows by cost descending (ties by row; bitonic sort of
+// plan::row_key), exclusive scans of items and partial slots in that order, items written from
+// the head's first item on.
 __global__ __launch_bounds__(kPlanThreads) void plan_rows_kernel(
     const int32_t* __restrict__ row_ptr, int32_t n_blk, const int32_t* __restrict__ hdr,
-    const int32_t* __restrict__ head_item_off, const int32_t* __restrict__ head_slot_base,
+    const int32_t* __restrict__ head_off, const int32_t* __restrict__ head_slot_base,
     int4* __restrict__ items, int32_t* __restrict__ done) {
     __shared__ int32_t cost[kMaxBlocks], ord[kMaxBlocks], ipos[kMaxBlocks], spos[kMaxBlocks];
     __shared__ int32_t part_i[kPlanThreads], part_s[kPlanThreads];
@@ -134,13 +149,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_rows_kernel(
     const int32_t Kc = hdr[kHdrKc];
     for (int i = t; i < n_blk; i += kPlanThreads) cost[i] = row_ptr[base + i + 1] - row_ptr[base + i];
     __syncthreads();
-    // rows by cost descending, ties by row index: bitonic sort of one 32-bit word per row,
-    // (kMaxBlocks - cost) above the 12-bit row index, padding words last
     int P2 = 2;
     while (P2 < n_blk) P2 <<= 1;
     uint32_t* key = (uint32_t*)ord;
     for (int i = t; i < P2; i += kPlanThreads)
-        key[i] = i < n_blk ? ((uint32_t)(kMaxBlocks - cost[i]) << 12) | (uint32_t)i : 0xffffffffu;
+        key[i] = i < n_blk ? plan::row_key(cost[i], i) : 0xffffffffu;
     __syncthreads();
     for (int kk = 2; kk <= P2; kk <<= 1)
         for (int jj = kk >> 1; jj > 0; jj >>= 1) {
@@ -156,17 +169,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_rows_kernel(
             }
             __syncthreads();
         }
-    for (int k = t; k < n_blk; k += kPlanThreads) ord[k] = (int32_t)(key[k] & 0xfffu);
+    for (int k = t; k < n_blk; k += kPlanThreads) ord[k] = plan::key_row(key[k]);
     __syncthreads();
     // exclusive scans (in rank order) of items per row and of partial slots per split row
     const int seg = (n_blk + kPlanThreads - 1) / kPlanThreads;
     const int lo = min(n_blk, t * seg), hi = min(n_blk, lo + seg);
     int32_t li = 0, ls = 0;
     for (int k = lo; k < hi; ++k) {
-        int32_t ni = (cost[ord[k]] + Kc - 1) / Kc;
-        ni = ni < 1 ? 1 : ni;
-        li += ni;
-        ls += ni > 1 ? ni : 0;
+        li += plan::row_items(cost[ord[k]], Kc);
+        ls += plan::row_slots(cost[ord[k]], Kc);
     }
     part_i[t] = li;
     part_s[t] = ls;
@@ -181,29 +192,102 @@ __global__ __launch_bounds__(kPlanThreads) void plan_rows_kernel(
     }
     int32_t ri = part_i[t] - li, rs = part_s[t] - ls;
     for (int k = lo; k < hi; ++k) {
-        int32_t ni = (cost[ord[k]] + Kc - 1) / Kc;
-        ni = ni < 1 ? 1 : ni;
         ipos[k] = ri;
         spos[k] = rs;
-        ri += ni;
-        rs += ni > 1 ? ni : 0;
+        ri += plan::row_items(cost[ord[k]], Kc);
+        rs += plan::row_slots(cost[ord[k]], Kc);
     }
     __syncthreads();
-    const int32_t ioff = head_item_off[h];
+    const int32_t ioff = head_off[h];
     const int32_t sbase = head_slot_base[h];
     for (int k = t; k < n_blk; k += kPlanThreads) {
         const int i = ord[k];
         const int32_t c = cost[i];
         const int32_t beg = row_ptr[base + i];
-        int32_t ni = (c + Kc - 1) / Kc;
-        ni = ni < 1 ? 1 : ni;
+        const int32_t ni = plan::row_items(c, Kc);
         const int32_t slot = ni > 1 ? sbase + spos[k] : -1;
         for (int s = 0; s < ni; ++s) {
             const int32_t b0 = beg + s * Kc;
             const int32_t b1 = min(beg + (s + 1) * Kc, beg + c);
             items[ioff + ipos[k] + s] = make_int4((int32_t)(base + i), b0, b1, slot);
         }
+        if (slot >= 0) done[slot] = 0;               // chunk counter of the split row
+    }
+}
+
+// Few-heads mode (plan.h).  One workgroup: every row of the layer (at most plan::kFewRows)
+// sorted by cost descending (ties by row; bitonic sort of plan::few_key in LDS), exclusive scans
+// of items and partial slots in that order, all items in queue 0, the other queues empty.
+__global__ __launch_bounds__(kPlanThreads) void plan_few_kernel(
+    const int32_t* __restrict__ row_ptr, int32_t rows, int32_t target,
+    int32_t* __restrict__ hdr, int4* __restrict__ items, int32_t* __restrict__ done) {
+    __shared__ uint32_t key[plan::kFewRows];
+    __shared__ int32_t part_i[kPlanThreads], part_s[kPlanThreads];
+    const int t = threadIdx.x;
+    const int32_t Kc = plan::chunk_size(row_ptr[rows], target);
+    int P2 = 2;
+    while (P2 < rows) P2 <<= 1;
+    for (int r = t; r < P2; r += kPlanThreads)
+        key[r] = r < rows ? plan::few_key(row_ptr[r + 1] - row_ptr[r], r) : 0xffffffffu;
+    __syncthreads();
+    for (int kk = 2; kk <= P2; kk <<= 1)
+        for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+            for (int i = t; i < P2; i += kPlanThreads) {
+                const int l = i ^ jj;
+                if (l > i) {
+                    const uint32_t x = key[i], y = key[l];
+                    if ((x > y) == ((i & kk) == 0)) {
+                        key[i] = y;
+                        key[l] = x;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    const int seg = (rows + kPlanThreads - 1) / kPlanThreads;
+    const int lo = min(rows, t * seg), hi = min(rows, lo + seg);
+    auto cost_at = [&](int k) {
+        const int r = plan::few_key_row(key[k]);
+        return row_ptr[r + 1] - row_ptr[r];
+    };
+    int32_t li = 0, ls = 0;
+    for (int k = lo; k < hi; ++k) {
+        li += plan::row_items(cost_at(k), Kc);
+        ls += plan::row_slots(cost_at(k), Kc);
+    }
+    part_i[t] = li;
+    part_s[t] = ls;
+    __syncthreads();
+    for (int off = 1; off < kPlanThreads; off <<= 1) {
+        const int32_t ai = t >= off ? part_i[t - off] : 0;
+        const int32_t as = t >= off ? part_s[t - off] : 0;
+        __syncthreads();
+        part_i[t] += ai;
+        part_s[t] += as;
+        __syncthreads();
+    }
+    int32_t ri = part_i[t] - li, rs = part_s[t] - ls;
+    for (int k = lo; k < hi; ++k) {
+        const int r = plan::few_key_row(key[k]);
+        const int32_t c = row_ptr[r + 1] - row_ptr[r], beg = row_ptr[r];
+        const int32_t ni = plan::row_items(c, Kc);
+        const int32_t slot = ni > 1 ? rs : -1;
+        for (int s = 0; s < ni; ++s) {
+            const int32_t b0 = beg + s * Kc;
+            const int32_t b1 = min(beg + (s + 1) * Kc, beg + c);
+            items[ri + s] = make_int4(r, b0, b1, slot);
+        }
         if (slot >= 0) done[slot] = 0;
+        ri += ni;
+        rs += plan::row_slots(c, Kc);
+    }
+    if (t == kPlanThreads - 1) {
+        hdr[kHdrKc] = Kc;
+        for (int q = 0; q < kNQ; ++q) {
+            hdr[kHdrQStart + q] = q == 0 ? 0 : ri;       // the last thread ends at the total
+            hdr[kHdrQLen + q] = q == 0 ? ri : 0;
+            hdr[kHdrCtr + 32 * q] = 0;
+        }
     }
 }
 
@@ -675,17 +759,22 @@ bsa_status launch_plan(const int32_t* row_ptr, int32_t batch, int32_t heads, int
     const AttnLayout L = attn_layout(batch, heads, D, g, slots);
     unsigned char* w = (unsigned char*)ws;
     int32_t* hdr = (int32_t*)(w + L.hdr);
-    int32_t* head_item_off = (int32_t*)(w + L.head_item_off);
+    int32_t* head_off = (int32_t*)(w + L.head_seg);
     int32_t* head_slot_base = (int32_t*)(w + L.head_slot_base);
     int4* items = (int4*)(w + L.items);
     int32_t* done = (int32_t*)(w + L.done);
     const int32_t nbh = batch * heads;
+    if (plan::few_heads(nbh, g.n_blk)) {
+        hipLaunchKernelGGL(plan_few_kernel, dim3(1), dim3(kPlanThreads), 0, s, row_ptr,
+                           nbh * g.n_blk, 2 * slots, hdr, items, done);
+        return check_launch("plan_few");
+    }
     hipLaunchKernelGGL(plan_global_kernel, dim3(1), dim3(kPlanThreads), 0, s, row_ptr, g.n_blk,
-                       nbh, 2 * slots, hdr, head_item_off, head_slot_base);
+                       nbh, 2 * slots, hdr, head_off, head_slot_base);
     bsa_status st = check_launch("plan_global");
     if (st != BSA_OK) return st;
     hipLaunchKernelGGL(plan_rows_kernel, dim3(nbh), dim3(kPlanThreads), 0, s, row_ptr, g.n_blk,
-                       hdr, head_item_off, head_slot_base, items, done);
+                       hdr, head_off, head_slot_base, items, done);
     return check_launch("plan_rows");
 }
 

@@ -5,6 +5,7 @@
 #pragma once
 
 #include "bsa_internal.h"
+#include "plan.h"
 
 namespace bsa {
 namespace {
@@ -12,45 +13,27 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kNQ = 8;             // XCD queues (MI355X: 8 XCDs)
+using plan::kNQ;
+using plan::kMaxHeads;
+using plan::kMaxBlocks;
+using plan::kKcMin;
 constexpr int kPlanThreads = 1024;
-constexpr int kMaxHeads = 2048;    // batch * heads supported by the planner
-constexpr int kMaxBlocks = 4096;   // n_blk supported by the planner
 static_assert(kMaxBlocks <= 4096, "the planner packs a row index into 12 bits");
-constexpr int kKcMin = 8;          // smallest chunk (blocks) a row is split into
 constexpr float kRescaleThresh = 8.0f;   // log2 units the running max may lag
 
-struct AttnLayout {
-    size_t hdr, head_item_off, head_slot_base, items, done, part_o, part_ml, total;
-    int64_t max_items, max_slots;
-};
+using AttnLayout = plan::Layout;
 
-// header ints: [0] Kc, [16 + 32 q] queue counters (128 B apart), [8 .. 8+kNQ) qstart,
-// [272 ..) qlen
+// header ints: [0] Kc, [8 .. 8 + kNQ) queue starts, [32 + 32 q] queue counters (128 B apart),
+// [32 + 32 kNQ ..) queue lengths
 constexpr int kHdrKc = 0;
 constexpr int kHdrQStart = 8;
 constexpr int kHdrCtr = 32;         // + 32*q
 constexpr int kHdrQLen = 32 + 32 * kNQ;
-constexpr int kHdrInts = kHdrQLen + kNQ;
+static_assert(plan::kHdrInts == kHdrQLen + kNQ, "header size");
 
 inline AttnLayout attn_layout(int32_t batch, int32_t heads, int32_t D, const Geometry& g,
-                       int slots) {
-    AttnLayout L;
-    const int64_t bh = (int64_t)batch * heads;
-    const int64_t rows = bh * g.n_blk;
-    const int64_t target = 2 * (int64_t)slots;
-    L.max_items = rows + target;
-    L.max_slots = 2 * target;
-    size_t off = 0;
-    L.hdr = off;            off = align_up(off + kHdrInts * 4, 256);
-    L.head_item_off = off;  off = align_up(off + bh * 4, 256);
-    L.head_slot_base = off; off = align_up(off + bh * 4, 256);
-    L.items = off;          off = align_up(off + L.max_items * 16, 256);
-    L.done = off;           off = align_up(off + L.max_slots * 4, 256);
-    L.part_o = off;         off = align_up(off + (size_t)L.max_slots * g.B * D * 4, 256);
-    L.part_ml = off;        off = align_up(off + (size_t)L.max_slots * g.B * 2 * 4, 256);
-    L.total = off;
-    return L;
+                              int slots) {
+    return plan::workspace_layout((int64_t)batch * heads, g.n_blk, g.B, D, slots);
 }
 
 __device__ __forceinline__ int xcc_id() {
