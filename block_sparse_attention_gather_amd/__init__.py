@@ -91,6 +91,9 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libbsa.so not built at {LIB_PATH}; run "
                           "`python -m block_sparse_attention_gather_amd.build`")
+    # torch first: it loads its own HIP runtime, and libbsa's HIP dependency must bind to that
+    # same runtime (a second runtime loaded ahead of it finds no device)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, F64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_double, ctypes.c_float,
                             ctypes.c_size_t)
