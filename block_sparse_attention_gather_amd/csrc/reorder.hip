@@ -89,9 +89,10 @@ void launch_dir(const uint4* sp, uint4* dp, const GridArgs& ga, dim3 grid, int32
 // heads fastest, so the workgroups in flight together read whole raster token rows of all
 // heads rather than one piece of each; blockIdx.y = b) and, each output
 // optional, writes them as the contiguous tiled block (pad rows zero), sums every column over
-// the block's real rows in fp64 (pooled[bh][j] = column sums / real rows; the sums of bf16
-// values are exact in fp64 for the value ranges involved, so the means equal a separate
-// pooling pass bit for bit), and with FP8 writes the block's E4M3 codes and scale exactly as
+// the block's real rows in fp64 (pooled[bh][j] = column sums / real rows; a sum of at most
+// 128 bf16 values whose nonzero magnitudes lie within a factor 2^38 of each other is exact in
+// fp64 in any order, so for such columns the means equal a separate pooling pass bit for
+// bit), and with FP8 writes the block's E4M3 codes and scale exactly as
 // the per-block quantization of the tiled tensor does (amax over the block, pad rows zero).
 template <int D, int B, bool FP8>
 __global__ __launch_bounds__(kReorderThreads) void reorder_pool_kernel(

@@ -101,8 +101,11 @@ BSA_API bsa_status bsa_reorder(const void* src, void* dst, const bsa_shape* shap
  * output may be NULL (at least one must be set):
  *   dst       as bsa_reorder(inverse = 0): tiled bf16 [batch, heads, Npad, D], pad rows zero;
  *   pooled    fp64 [batch, heads, n_blk, D]: pooled[b][h][j] = mean of the tiled rows j*block ..
- *             min((j+1)*block, N) - 1 (the block's real tokens), bit-identical to the pooling
- *             inside bsa_score_and_route;
+ *             min((j+1)*block, N) - 1 (the block's real tokens).  Bit-identical to the pooling
+ *             inside bsa_score_and_route whenever, in every column of a block, the nonzero
+ *             bf16 values lie within a factor 2^38 of each other: every fp64 partial sum of
+ *             at most 128 such values is then exact, whatever the order.  For wider spreads
+ *             the two sums may round differently in the last bit of the mean;
  *   x8, x8_scales (both or neither): the E4M3 codes and per-block scales that
  *             bsa_quantize_fp8(v_layout = 0) writes for the tiled tensor (head_dim 128 and
  *             block 128 only, else BSA_ERR_UNSUPPORTED).
