@@ -4,8 +4,9 @@ TEST INFRASTRUCTURE ONLY: imported by the tests and the bench's CPU leg, never b
 path; shares no code with the HIP kernels.
 
 Source: the PSA page ("Parameterized Stripe Attention for Efficient Video Generation",
-"Approach"): video DiT attention maps show periodic diagonal stripes, covered by one
-six-parameter mask M(Tw, To, Ts, Sw, So, Ss) per head and run by one block-sparse kernel.  The
+"Approach"): the attention of video DiTs concentrates on bands that repeat along the
+diagonal, which one mask of six parameters M(Tw, To, Ts, Sw, So, Ss) per head covers, executed
+by a single block-sparse kernel.  The
 page names the parameters but does not define them.  Reading used here (T = temporal,
 S = spatial; w = stripe width, o = offset, s = period), on the block grid of the 3D-tile
 order:
