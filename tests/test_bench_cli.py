@@ -55,7 +55,7 @@ def test_traffic_figures_belong_to_one_kernel_mode_and_workload():
         else:
             assert got is None                                  # taken on another kernel
     assert bench.attn_traffic("small", "bf16") is None            # never measured
-    assert bench.attn_traffic("wan480p", "fp8-rne") is None
+    assert bench.attn_traffic("wan720p", "fp8-rne") is None
 
 
 def test_traffic_lookup_rejects_a_changed_source(monkeypatch):
