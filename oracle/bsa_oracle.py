@@ -27,7 +27,6 @@ Everything here is fp64.  bf16 inputs arrive as uint16 bit patterns and are wide
 """
 from __future__ import annotations
 
-import math
 import os
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass

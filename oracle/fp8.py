@@ -30,7 +30,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .bsa_oracle import num_blocks, padded_len, widen_bf16
+from .bsa_oracle import num_blocks, widen_bf16
 
 E4M3_MAX = 448.0
 P_OFFSET_LOG2 = 8          # probabilities are cast as 2^8 * exp(l - m)

@@ -19,7 +19,7 @@ import block_sparse_attention_gather_amd as bsa
 import oracle as O
 from workloads import bf16_bits_from_f64, f64_from_bf16_bits
 
-from gpu_common import attn_scale, bf16_f64, to_bits
+from gpu_common import attn_scale, bf16_f64
 
 pytestmark = pytest.mark.gpu
 

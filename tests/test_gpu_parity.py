@@ -8,7 +8,6 @@ import math
 
 import numpy as np
 import pytest
-import torch
 
 import block_sparse_attention_gather_amd as bsa
 import oracle as O

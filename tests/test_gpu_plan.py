@@ -4,7 +4,6 @@ library's sequential host planner (plan_host.h, compiled for the CPU by tests/pl
 the same CSR: chunk size, queue starts and lengths, every work item, partial-slot bases.
 Cases: routed masks, every row dense (split rows), one dense head among sparse ones; 6 heads
 (few-heads mode, one queue) and 20 heads (head mode, XCD queues)."""
-import math
 
 import numpy as np
 import pytest

@@ -1,7 +1,6 @@
 """GPU tests of the static periodic-stripe masks (bsa_stripe_mask) through the C ABI, against
 the oracle's reading of the PSA page's six-parameter mask, and of the attention kernel run on
 them (the second workload of bsa_sparse_attn_fwd).  CSRs must be bit-identical."""
-import math
 
 import numpy as np
 import pytest
@@ -9,7 +8,7 @@ import torch
 
 import block_sparse_attention_gather_amd as bsa
 import oracle as O
-from workloads import Config, CONFIGS, gen_qkv
+from workloads import Config, gen_qkv
 
 from gpu_common import attn_scale, bf16_f64, grid_of, to_bits, to_dev
 

@@ -4,7 +4,6 @@ import math
 import os
 
 import numpy as np
-import pytest
 from scipy.special import softmax
 
 import oracle as O

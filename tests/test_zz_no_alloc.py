@@ -4,7 +4,6 @@ raw through the C ABI twice in a row, the second time on a smaller input, each o
 bit-identical to bsa_sparse_attn_fwd's on the same inputs (and therefore inside the parity
 bars: max-abs 2e-2, mean-abs 2e-3, LSE 1e-3 against the oracle, checked too)."""
 import ctypes
-import math
 
 import numpy as np
 import pytest
