@@ -472,9 +472,11 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
             // Q is in registers before the first LDS DMA of the item is issued, so the only
             // vector-memory operations in flight inside the block loop are the DMA tiles
             wait_vmcnt(0);
-            // first key block of the item into LDS
-            dma_tile<D, B, false>(kbase + (int64_t)ld_const(a.col_idx, it.y) * B * D, ks_addr, wv,
-                                  lane);
+            // first key block of the item into LDS (a row without blocks reads none and is
+            // written as zeros below, like a pad row)
+            if (it.y < it.z)
+                dma_tile<D, B, false>(kbase + (int64_t)ld_const(a.col_idx, it.y) * B * D,
+                                      ks_addr, wv, lane);
 
             f32x16 o[Tl::NDT];
 #pragma unroll

@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnF8Args a) {
                 }
             }
             wait_vmcnt(0);
-            {
+            if (it.y < it.z) {              // (a row without blocks is written as zeros)
                 const uint8_t* k0 = uniform_ptr8(kbase + (int64_t)ld_const(a.col_idx, it.y) * B * D);
 #pragma unroll
                 for (int u = 0; u < kF8TI; ++u) dma8_part(k0, ks_addr, wv, lane, u);

@@ -216,10 +216,11 @@ BSA_API size_t bsa_attn_workspace_bytes(const bsa_shape* shape, const bsa_grid* 
  * Pad query rows (p >= N) of out_t and lse are written with zeros.
  * q_t, k_t, v_t, out_t: tiled bf16 [batch, heads, Npad, D]; lse: [batch, heads, Npad] fp32 or
  * NULL.  The pad rows (positions N..Npad-1) of k_t and v_t are read and must hold finite
- * values (bsa_reorder writes zeros there); their logits are masked out.  Every row must keep
- * at least one block; col_idx values must lie in [0, n_blk) and be distinct within a row
- * (bsa_score_and_route guarantees both; other CSRs are the caller's responsibility and are
- * not checked on the device).
+ * values (bsa_reorder writes zeros there); their logits are masked out.  A row that keeps no
+ * block (row_ptr[r] == row_ptr[r+1]; bsa_score_and_route never emits one) has no softmax: its
+ * rows of out_t and lse are written with zeros, like pad rows.  col_idx values must lie in
+ * [0, n_blk) and be distinct within a row (bsa_score_and_route guarantees it; other CSRs are
+ * the caller's responsibility and are not checked on the device).
  * The heavy-row scheduler is persistent: work items are built on the device from the CSR row
  * lengths, long rows are split and their partial results merged in a fixed order, so the
  * output is bitwise deterministic.

@@ -95,12 +95,14 @@ def test_guard_regions_untouched():
 
 
 def random_csr(rng, heads, n, kinds):
-    """CSR over heads * n rows; kinds cycles per row: 'full', 'one', 'rand'."""
+    """CSR over heads * n rows; kinds cycles per row: 'full', 'one', 'rand', 'empty'."""
     rp = [0]
     cols = []
     for r in range(heads * n):
         kind = kinds[r % len(kinds)]
-        if kind == "full":
+        if kind == "empty":
+            c = np.zeros(0, np.int64)
+        elif kind == "full":
             c = np.arange(n)
         elif kind == "one":
             c = np.array([rng.integers(n)])
@@ -162,3 +164,59 @@ def test_reorder_batched_any_head_dim(D):
     assert np.array_equal(to_bits(xt), ref)
     back = bsa.reorder(xt, grid, inverse=True)
     assert np.array_equal(to_bits(back), x)
+
+
+@pytest.mark.parametrize("D,B,fp8", [(128, 128, False), (64, 64, False), (128, 128, True)],
+                         ids=["d128", "d64", "fp8"])
+def test_attention_empty_rows(D, B, fp8):
+    """Rows that keep no block (every 4th row and the last row of the layer) are written as
+    zeros, output and LSE, like pad rows; the other rows match the oracle as usual."""
+    cfg = Config("empty", 4, 12, 21, 2, D, B, (4, 4, 8) if B == 128 else (2, 4, 8), 1.0, 1, 36)
+    q, k, v = gen_qkv(cfg, gains=np.full(2, 1.5))
+    grid = grid_of(cfg)
+    n, N = grid.n_blk, cfg.N
+    rng = np.random.default_rng(37)
+    rp, ci = random_csr(rng, 2, n, ["empty", "rand", "full", "one"])
+    empty = [r for r in range(2 * n) if r % 4 == 0 or r == 2 * n - 1]
+    keep = [np.sort(ci[rp[r]:rp[r + 1]]) if r not in empty else np.zeros(0, np.int64)
+            for r in range(2 * n)]
+    rp = np.concatenate([[0], np.cumsum([len(x) for x in keep])]).astype(np.int64)
+    ci = np.concatenate(keep).astype(np.int64)
+    print(f"[gpu] empty rows D={D} B={B} fp8={fp8} rows={2 * n} empty={len(empty)}", flush=True)
+    q_t, k_t, v_t = (bsa.reorder(to_dev(x), grid) for x in (q, k, v))
+    rp_d = torch.from_numpy(rp.astype(np.int32)).to("cuda:0")
+    ci_d = torch.from_numpy(ci.astype(np.int32)).to("cuda:0")
+    sc = attn_scale(D)
+    if fp8:
+        q8, qs = bsa.quantize_fp8(q_t, grid)
+        k8, ks = bsa.quantize_fp8(k_t, grid)
+        v8, vs = bsa.quantize_fp8(v_t, grid, v_layout=True)
+        out_t, lse = bsa.sparse_attn_fwd_fp8(q8, qs, k8, ks, v8, vs, rp_d, ci_d, grid, sc)
+    else:
+        out_t, lse = bsa.sparse_attn_fwd(q_t, k_t, v_t, rp_d, ci_d, grid, sc)
+    torch.cuda.synchronize()
+    got = bf16_f64(out_t)
+    lse_h = lse.cpu().numpy().astype(np.float64)
+    for r in empty:
+        hh, i = divmod(r, n)
+        assert np.all(got[0, hh, i * B:(i + 1) * B] == 0) and np.all(lse_h[0, hh, i * B:(i + 1) * B] == 0)
+    assert np.all(got[:, :, N:] == 0)
+    if fp8:
+        # the non-empty rows against the FP8 bound are covered by test_gpu_fp8; here only
+        # that they were computed (finite, not all zero)
+        for r in range(2 * n):
+            if r in empty:
+                continue
+            hh, i = divmod(r, n)
+            blk = got[0, hh, i * B:min((i + 1) * B, N)]
+            assert np.all(np.isfinite(blk)) and np.any(blk != 0)
+        return
+    for hh in range(2):
+        blocks = [i for i in range(n) if hh * n + i not in empty]
+        Oref, Lref = O.sparse_attn(to_bits(q_t), to_bits(k_t), to_bits(v_t), rp, ci, N, B, sc,
+                                   heads=[hh], qblocks=blocks)
+        for i in blocks:
+            lo, hi = i * B, min((i + 1) * B, N)
+            d = np.abs(got[0, hh, lo:hi] - Oref[0, hh, lo:hi])
+            assert d.max() <= 2e-2, (hh, i, d.max())
+            assert np.abs(lse_h[0, hh, lo:hi] - Lref[0, hh, lo:hi]).max() <= 1e-3
