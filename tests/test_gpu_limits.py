@@ -9,6 +9,8 @@
   (4095, the top of the planner's 12-bit row field).
 * 2048 batch x heads (the planner's head limit): routing and attention over 2048 heads of a
   tiny grid, every mask row checked and sampled heads' outputs against the oracle.
+* The FP8 kernel on the same 4096-block CSR, both probability casts, against the oracle's
+  derived bounds.
 * One past each limit (4097 blocks, 2049 heads) is refused on the host before any launch.
 Bars as everywhere: output max-abs 2e-2 and mean-abs 2e-3, LSE 1e-3, masks per R15.
 """
@@ -147,3 +149,66 @@ def test_one_past_each_limit_is_refused():
     ci = torch.zeros(g.n_blk, dtype=torch.int32, device=dev)
     with pytest.raises(bsa.BsaError, match="exceeds"):
         bsa.sparse_attn_fwd(x, x, x, rp, ci, g, 0.125)
+
+
+@pytest.mark.parametrize("expcast", [False, True], ids=["rne", "expcast"])
+def test_fp8_attention_4096_blocks_split_rows(expcast):
+    """The FP8 kernel at 4096 key blocks a row with the same CSR as above (dense rows split into
+    about 200 chunks and merged): outputs within the oracle's cast bound plus the fp32 and bf16
+    terms (tests/fp8_support.fp8_out_tol), LSE within 1e-3 (plus the ExpCast bound)."""
+    from oracle import fp8 as F
+    from fp8_support import fp8_out_tol
+    B = D = 128
+    n = 4096
+    N = n * B - 45
+    grid = bsa.Grid(1, 1, N, (1, 1, B), B)
+    rng = np.random.default_rng(65)
+    print(f"[gpu] limits: fp8 attention expcast={expcast} N={N} n_blk={n}", flush=True)
+    tens = []
+    for _ in range(3):
+        t = np.zeros((1, 1, grid.Npad, D))
+        t[0, 0, :N] = rng.standard_normal((N, D))
+        tens.append(torch.from_numpy(bf16_bits_from_f64(t).view(np.int16)).view(
+            torch.bfloat16).to("cuda:0"))
+    q_t, k_t, v_t = tens
+    rows = [np.arange(n) if i in (n // 2, n - 1) else np.unique([0, i, n - 1]) for i in range(n)]
+    rp = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int64)
+    ci = np.concatenate(rows).astype(np.int64)
+    rp_d = torch.from_numpy(rp.astype(np.int32)).to("cuda:0")
+    ci_d = torch.from_numpy(ci.astype(np.int32)).to("cuda:0")
+    q8, qs = bsa.quantize_fp8(q_t, grid)
+    k8, ks = bsa.quantize_fp8(k_t, grid)
+    v8, vs = bsa.quantize_fp8(v_t, grid, v_layout=True)
+    sc = attn_scale(D)
+    out, lse = bsa.sparse_attn_fwd_fp8(q8, qs, k8, ks, v8, vs, rp_d, ci_d, grid, sc,
+                                       expcast=expcast)
+    torch.cuda.synchronize()
+    qc, qsr = F.quantize_rows(to_bits(q_t), B)
+    kc, ksr = F.quantize_rows(to_bits(k_t), B)
+    vc, vsr = F.quantize_v(to_bits(v_t), B)
+    qd, kd, vd = (F.dequantize_rows(qc, qsr, B), F.dequantize_rows(kc, ksr, B),
+                  F.dequantize_v(vc, vsr))
+    check = [(0, 0, i) for i in (0, 1, n // 2, n - 2, n - 1)]
+    if expcast:
+        bnd = F.expcast_error_bound(qd, kd, vd, rp, ci, N, B, sc, check)
+    else:
+        bo = F.attn_error_bound(qd, kd, vd, rp, ci, N, B, sc, check)
+        bnd = {r: (bo[r], np.zeros(bo[r].shape[0])) for r in check}
+    wabs = F.abs_weighted_v(qd, kd, vd, rp, ci, N, B, sc, check)
+    Oref, Lref = O.sparse_attn(qd, kd, vd, rp, ci, N, B, sc, heads=[0],
+                               qblocks=[i for _, _, i in check])
+    got = bf16_f64(out)
+    lse_h = lse.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for r in check:
+        i = r[2]
+        lo, hi = i * B, min((i + 1) * B, N)
+        ref = Oref[0, 0, lo:hi]
+        tol = fp8_out_tol(bnd[r][0], ref, wabs[r])
+        err = np.abs(got[0, 0, lo:hi] - ref)
+        assert np.all(err <= tol), (i, float((err / tol).max()))
+        worst = max(worst, float((err / tol).max()))
+        dl = np.abs(lse_h[0, 0, lo:hi] - Lref[0, 0, lo:hi])
+        assert np.all(dl <= bnd[r][1] + 1e-3), (i, float(dl.max()))
+    assert np.all(got[:, :, N:] == 0)
+    print(f"[gpu]   rows {[i for _, _, i in check]}: worst err/bound {worst:.3f}", flush=True)
