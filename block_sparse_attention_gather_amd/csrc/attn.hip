@@ -525,6 +525,10 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
                     }
                     pin_pipeline<NM, 1>();
                 }
+                // every S^T MFMA is issued before the V wait (the last ones would otherwise be
+                // sunk below it)
+#pragma unroll
+                for (int tt = 0; tt < Tl::NKT; ++tt) keep_issued(s[tt]);
                 wait_vm<0>();                            // V_e landed
                 barrier_lds();                           // V_e visible; every wave done with K_e
                 // pad keys of a short last block

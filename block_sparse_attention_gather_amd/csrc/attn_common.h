@@ -101,6 +101,12 @@ __device__ __forceinline__ void barrier_lds() {
     __builtin_amdgcn_s_barrier();
 }
 
+// An empty statement that takes an MFMA result, placed before a wait for a tile: the MFMAs that
+// produce it are then issued ahead of the wait.  Without such a use the compiler may sink them
+// (they touch no memory) below the wait and the barrier after it, and the tile's latency is no
+// longer covered by matrix work.
+__device__ __forceinline__ void keep_issued(const f32x16& x) { asm volatile("" ::"v"(x)); }
+
 // Value held by lane l ^ 32 (the other half of the wavefront), via v_permlane32_swap.
 __device__ __forceinline__ float other_half(float x) {
     const unsigned u = __builtin_bit_cast(unsigned, x);

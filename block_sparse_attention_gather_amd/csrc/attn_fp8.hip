@@ -208,6 +208,11 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnF8Args a) {
 #pragma unroll
                     for (int i = 0; i < 8; ++i) s[i >> 1] = mfma_f8(kf[i], qf[i & 1], s[i >> 1]);
                 }
+                // every S^T MFMA is issued before the V wait: without this use the compiler sank
+                // all eight below the wait and the barrier, so the V tile's arrival was not
+                // covered by matrix work (measured 3.4-4.3 % slower)
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) keep_issued(s[tt]);
                 wait_vm<0>();                            // V_e landed
                 barrier_lds();                           // V_e visible; every wave done with K_e
                 if (more)
