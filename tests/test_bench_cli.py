@@ -66,21 +66,33 @@ def test_traffic_lookup_rejects_a_changed_source(monkeypatch):
     assert bench.attn_traffic("tiny", t["mode"]) is None
 
 
-def test_kernel_key_covers_per_source_compiler_options():
-    """A per-source compiler option is part of the kernel the traffic figures belong to: the key
-    of a source with options differs from the plain sha256 of the file, and every option set
-    names a source the build compiles."""
-    import hashlib
+def test_kernel_key_covers_headers_and_compiler_options(tmp_path, monkeypatch):
+    """A figure belongs to the kernel as compiled: its source, the library headers it includes
+    and its per-source compiler options.  Changing a shared header changes the key of exactly the
+    sources that include it; dropping the options changes the key of exactly the sources that
+    have them."""
+    import shutil
     from block_sparse_attention_gather_amd import build as B
     for src, flags in B.SOURCE_FLAGS.items():
         assert src in B.SOURCES and flags
-        with open(os.path.join(B.CSRC, src), "rb") as fh:
-            plain = hashlib.sha256(fh.read()).hexdigest()
-        assert bench.src_sha256(src) != plain
-    for src in B.SOURCES:
-        if src not in B.SOURCE_FLAGS:
-            with open(os.path.join(B.CSRC, src), "rb") as fh:
-                assert bench.src_sha256(src) == hashlib.sha256(fh.read()).hexdigest()
+    for src in ("attn.hip", "attn_fp8.hip"):
+        assert {"attn_common.h", "plan.h"} <= set(bench.local_headers(src))
+    before = {s: bench.src_sha256(s) for s in B.SOURCES}
+    root = tmp_path / "r"
+    csrc = root / "block_sparse_attention_gather_amd" / "csrc"
+    shutil.copytree(B.CSRC, csrc)
+    monkeypatch.setattr(bench, "ROOT", str(root))
+    assert {s: bench.src_sha256(s) for s in B.SOURCES} == before    # same text, same keys
+    with open(csrc / "attn_common.h", "a") as fh:
+        fh.write("\n// changed\n")
+    after = {s: bench.src_sha256(s) for s in B.SOURCES}
+    for s in B.SOURCES:
+        assert (after[s] != before[s]) == ("attn_common.h" in bench.local_headers(s)), s
+    flagged = set(B.SOURCE_FLAGS)
+    monkeypatch.setattr(B, "SOURCE_FLAGS", {})
+    plain = {s: bench.src_sha256(s) for s in B.SOURCES}
+    for s in B.SOURCES:
+        assert (plain[s] != after[s]) == (s in flagged), s
 
 
 def test_host_info_describes_the_cpu():
