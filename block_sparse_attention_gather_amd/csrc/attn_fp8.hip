@@ -273,7 +273,9 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnF8Args a) {
                 // element e of key tile 2 kc + t
                 v8i32 pf[2];
                 const float off = 8.0f - m;
-                const float c8 = XC ? 8.0f * c_blk * (1.0f / 65535.0f) : 0.f;
+                // (floored like c_blk, so that the masked pad keys stay at -inf whatever the
+                // denormal mode)
+                const float c8 = XC ? fmaxf(8.0f * c_blk * (1.0f / 65535.0f), 1.17549435e-38f) : 0.f;
                 const float k8 = XC ? (8.0f * off + 56.0f - 0.00390625f) * (1.0f / 65535.0f) : 0.f;
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc)

@@ -27,8 +27,9 @@ def _tiled(cfg, zero_block=None):
     q, k, v = gen_qkv(cfg, gains=np.full(cfg.heads, 1.5))
     grid = grid_of(cfg)
     q_t, k_t, v_t = (bsa.reorder(to_dev(x), grid) for x in (q, k, v))
-    if zero_block is not None:
-        hh, j = zero_block
+    blocks = [] if zero_block is None else (
+        zero_block if isinstance(zero_block, list) else [zero_block])
+    for hh, j in blocks:
         for t in (q_t, k_t):
             t[0, hh, j * cfg.block:(j + 1) * cfg.block] = 0
     return grid, q_t, k_t, v_t
@@ -85,13 +86,18 @@ def test_fused_reorder_quantization():
 
 
 @pytest.mark.parametrize("expcast", [False, True], ids=["rne", "expcast"])
-@pytest.mark.parametrize("grid3,heads,routed,seed", [((4, 12, 21), 3, True, 82),
-                                                     ((6, 24, 32), 1, False, 83)],
-                         ids=["routed", "split_full"])
-def test_fp8_attention_within_bound(grid3, heads, routed, seed, expcast):
+@pytest.mark.parametrize("grid3,heads,routed,seed,zero", [
+    ((4, 12, 21), 3, True, 82, None),
+    ((6, 24, 32), 1, False, 83, None),
+    # Q and K of whole blocks zero (scale 0, so the softmax multiplier is floored): the last
+    # block of head 1, which also holds the 16 pad keys of the ragged tail, and a middle block
+    # of head 0; every row takes every block
+    ((4, 12, 21), 2, False, 84, [(1, 7), (0, 3)])],
+    ids=["routed", "split_full", "zero_blocks"])
+def test_fp8_attention_within_bound(grid3, heads, routed, seed, zero, expcast):
     T, H, W = grid3
     cfg = Config("f8a", T, H, W, heads, 128, 128, (4, 4, 8), 0.9, 2, seed)
-    grid, q_t, k_t, v_t = _tiled(cfg)
+    grid, q_t, k_t, v_t = _tiled(cfg, zero_block=zero)
     n, N, B = grid.n_blk, cfg.N, cfg.block
     if routed:
         rp, ci, nnz = bsa.score_and_route(q_t, k_t, grid, cfg.top_p, cfg.k_floor)
