@@ -98,7 +98,7 @@ def test_fp8_attention_within_bound(grid3, heads, routed, seed, zero, expcast):
     T, H, W = grid3
     cfg = Config("f8a", T, H, W, heads, 128, 128, (4, 4, 8), 0.9, 2, seed)
     grid, q_t, k_t, v_t = _tiled(cfg, zero_block=zero)
-    n, N, B = grid.n_blk, cfg.N, cfg.block
+    n = grid.n_blk
     if routed:
         rp, ci, nnz = bsa.score_and_route(q_t, k_t, grid, cfg.top_p, cfg.k_floor)
     else:                                         # every row full: long rows are split
@@ -111,9 +111,18 @@ def test_fp8_attention_within_bound(grid3, heads, routed, seed, zero, expcast):
     sc = attn_scale(128)
     out, lse = bsa.sparse_attn_fwd_fp8(q8, qs, k8, ks, v8, vs, rp, ci, grid, sc, expcast=expcast)
     torch.cuda.synchronize()
-    nz = int(nnz.item())
-    print(f"[gpu] fp8 attention {T}x{H}x{W} heads={heads} n_blk={n} nnz={nz} "
+    print(f"[gpu] fp8 attention {T}x{H}x{W} heads={heads} n_blk={n} nnz={int(nnz.item())} "
           f"expcast={expcast}", flush=True)
+    _check_fp8(out, lse, q_t, k_t, v_t, rp, ci, nnz, cfg, sc, expcast)
+
+
+def _check_fp8(out, lse, q_t, k_t, v_t, rp, ci, nnz, cfg, sc, expcast):
+    """Every row of every (batch, head) within the oracle's cast bound (ExpCast or exact cast)
+    of the exact attention over the dequantized inputs; pad rows zero."""
+    N, B = cfg.N, cfg.block
+    nb, heads = q_t.shape[0], q_t.shape[1]
+    n = -(-N // B)
+    nz = int(nnz.item())
     rp_h = rp.cpu().numpy().astype(np.int64)
     ci_h = ci[:nz].cpu().numpy().astype(np.int64)
     qc, qsr = F.quantize_rows(to_bits(q_t), B)
@@ -122,7 +131,7 @@ def test_fp8_attention_within_bound(grid3, heads, routed, seed, zero, expcast):
     qd, kd, vd = (F.dequantize_rows(qc, qsr, B), F.dequantize_rows(kc, ksr, B),
                   F.dequantize_v(vc, vsr))
     Oref, Lref = O.sparse_attn(qd, kd, vd, rp_h, ci_h, N, B, sc)
-    rows = [(0, hh, i) for hh in range(heads) for i in range(n)]
+    rows = [(bi, hh, i) for bi in range(nb) for hh in range(heads) for i in range(n)]
     if expcast:
         bnd = F.expcast_error_bound(qd, kd, vd, rp_h, ci_h, N, B, sc, rows)
     else:
@@ -132,18 +141,40 @@ def test_fp8_attention_within_bound(grid3, heads, routed, seed, zero, expcast):
     got = bf16_f64(out)
     lse_h = lse.cpu().numpy().astype(np.float64)
     worst = 0.0
-    for (_, hh, i) in rows:
+    for (bi, hh, i) in rows:
         lo, hi = i * B, min((i + 1) * B, N)
-        ref = Oref[0, hh, lo:hi]
-        tol = fp8_out_tol(bnd[(0, hh, i)][0], ref, wabs[(0, hh, i)])
-        err = np.abs(got[0, hh, lo:hi] - ref)
-        assert np.all(err <= tol), (hh, i, float((err / tol).max()))
+        ref = Oref[bi, hh, lo:hi]
+        tol = fp8_out_tol(bnd[(bi, hh, i)][0], ref, wabs[(bi, hh, i)])
+        err = np.abs(got[bi, hh, lo:hi] - ref)
+        assert np.all(err <= tol), (bi, hh, i, float((err / tol).max()))
         worst = max(worst, float((err / tol).max()))
-        dl = np.abs(lse_h[0, hh, lo:hi] - Lref[0, hh, lo:hi])
-        assert np.all(dl <= bnd[(0, hh, i)][1] + 1e-3), (hh, i, float(dl.max()))
+        dl = np.abs(lse_h[bi, hh, lo:hi] - Lref[bi, hh, lo:hi])
+        assert np.all(dl <= bnd[(bi, hh, i)][1] + 1e-3), (bi, hh, i, float(dl.max()))
     assert np.all(got[:, :, N:] == 0)
     # accuracy against the exact attention on the bf16 inputs (reported, not a bar)
     O16, _ = O.sparse_attn(to_bits(q_t), to_bits(k_t), to_bits(v_t), rp_h, ci_h, N, B, sc)
     d16 = np.abs(got[:, :, :N] - O16[:, :, :N])
     print(f"[gpu]   worst err/bound {worst:.3f}; vs bf16-input attention max-abs "
           f"{d16.max():.3e} mean-abs {d16.mean():.3e}", flush=True)
+
+
+@pytest.mark.parametrize("expcast", [False, True], ids=["rne", "expcast"])
+def test_fp8_attention_batch2(expcast):
+    """Batch 2 (two differently seeded fields, two heads each, ragged tail), routed by
+    bsa_score_and_route: every row of both batch entries within the cast bound."""
+    cfgs = [Config("f8b", 4, 12, 21, 2, 128, 128, (4, 4, 8), 0.9, 2, 95 + i) for i in range(2)]
+    qkv = [gen_qkv(c, gains=np.full(2, 1.5)) for c in cfgs]
+    cfg = cfgs[0]
+    grid = grid_of(cfg)
+    q_t, k_t, v_t = (bsa.reorder(to_dev(np.concatenate([x[j] for x in qkv], axis=0)), grid)
+                     for j in range(3))
+    rp, ci, nnz = bsa.score_and_route(q_t, k_t, grid, cfg.top_p, cfg.k_floor)
+    q8, qs = bsa.quantize_fp8(q_t, grid)
+    k8, ks = bsa.quantize_fp8(k_t, grid)
+    v8, vs = bsa.quantize_fp8(v_t, grid, v_layout=True)
+    sc = attn_scale(128)
+    out, lse = bsa.sparse_attn_fwd_fp8(q8, qs, k8, ks, v8, vs, rp, ci, grid, sc, expcast=expcast)
+    torch.cuda.synchronize()
+    print(f"[gpu] fp8 attention batch=2 heads=2 N={cfg.N} nnz={int(nnz.item())} "
+          f"expcast={expcast}", flush=True)
+    _check_fp8(out, lse, q_t, k_t, v_t, rp, ci, nnz, cfg, sc, expcast)
