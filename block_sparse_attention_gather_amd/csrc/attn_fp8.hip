@@ -16,8 +16,10 @@ namespace {
 // a lane fill the k-slots of its half-wave; the accumulator has the layout of the 32x32 bf16
 // product (element e of lane L: row 8(e/4) + 4(L/32) + e mod 4, column L mod 32), so
 // S^T = K Q^T leaves each lane one query and 16 keys per 32-key tile exactly as in the bf16
-// kernel.  Probabilities are 2^8 exp(l - m) with m the exact running maximum (rescaled as soon
-// as it grows), so every cast value lies in (0, 256].  Two casts:
+// kernel.  Probabilities are 2^8 exp(l - m) with m a running maximum that may lag the exact
+// one by up to kF8Lag = 0.75 (log2 units; it is raised, and O rescaled, only when a block's
+// maximum passes m + 0.75), so every cast value lies in (0, 2^8.75] and stays below E4M3's
+// largest finite value 448 (ExpCast code 126 at most).  Two casts:
 //   XC = false: exp2 in fp32, then E4M3 with round to nearest even; the row sum is the fp32
 //               sum of the uncast values;
 //   XC = true:  ExpCast (VC-Attention page, abstract: log-domain scores mapped to E4M3 codes
@@ -56,6 +58,7 @@ struct AttnF8Args {
 typedef int v8i32 __attribute__((ext_vector_type(8)));
 constexpr int kF8Row = 128;                 // bytes per LDS row (D or B fp8 values)
 constexpr int kF8TI = 4;                    // DMA instructions per wave per 16 KiB tile
+constexpr float kF8Lag = 0.75f;             // allowed lag of the running maximum (log2 units)
 
 // 16-byte chunk c of LDS row r is stored at chunk c ^ ((r / 2) mod 8).  The LDS serves the 16
 // lanes of a ds_read_b128 from 256 bytes of banks, i.e. two 128-byte rows: the operand reads
@@ -258,7 +261,9 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnF8Args a) {
                     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tt][r]);
                 mx = fmaxf(mx, other_half(mx));
                 const float mnew = mx * c_blk;
-                if (__any(mnew > m)) {
+                // (a lagging maximum rescales O rarely; measured 1-3 % faster than raising it
+                // with every larger block maximum)
+                if (__any(mnew > m + kF8Lag)) {
                     const float mn = fmaxf(m, mnew);
                     const float alpha = __builtin_amdgcn_exp2f(m - mn);
                     l *= alpha;
