@@ -10,12 +10,13 @@
 // load balancing moves heavy heads between GPUs - here the same problem is solved between the
 // compute units of one GPU):
 //   plan_global  one workgroup: chunk size Kc from nnz, per-head work, heads assigned to the
-//                8 XCD queues longest-first (each head's K/V then stays in one XCD's L2),
+//                8 XCD queues longest-first (each head's K/V then stays in one XCD's L2, or
+//                in a pair's when eight heads' K/V exceed the MALL and pairs share a queue),
 //                queue offsets, counters reset.
 //   plan_rows    one workgroup per head: rows ordered by cost descending (ties: row order),
 //                rows longer than Kc split into chunks, work items written in queue order.
 //   attn         persistent: each workgroup reads its XCD id, pops items from its own queue
-//                with an atomic counter, then steals from the other queues; every queue is
+//                (its pair's: the even XCD's) with an atomic counter, then steals from the other queues; every queue is
 //                visited once after it runs dry, so every workgroup exits.  A split row's
 //                chunks store unnormalised partials; the chunk that finishes last merges them
 //                in chunk order, so results do not depend on timing.
@@ -41,11 +42,12 @@ namespace {
 // ---------------------------------------------------------------------------------------
 // Head mode (plan.h).  One workgroup: Kc; per head its kept blocks, work items and partial
 // slots (a wavefront per head); heads ranked by cost (bitonic sort of plan::head_key in LDS)
-// and given longest-first to the least-loaded XCD queue; queue starts and lengths; every head's
-// first item (head_off) and first partial slot; queue counters reset.
+// and given longest-first to the least-loaded queue of those in use (every `group`-th);
+// queue starts and lengths; every head's first item (head_off) and first partial slot; queue
+// counters reset.
 __global__ __launch_bounds__(kPlanThreads) void plan_global_kernel(
     const int32_t* __restrict__ row_ptr, int32_t n_blk, int32_t nbh, int32_t target,
-    int32_t* __restrict__ hdr, int32_t* __restrict__ head_off,
+    int32_t group, int32_t* __restrict__ hdr, int32_t* __restrict__ head_off,
     int32_t* __restrict__ head_slot_base) {
     __shared__ int32_t hitems[kMaxHeads], hslots[kMaxHeads], horder[kMaxHeads];
     __shared__ uint64_t hkey[kMaxHeads];
@@ -101,15 +103,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_global_kernel(
     for (int r = t; r < nbh; r += kPlanThreads) horder[r] = plan::key_head(hkey[r]);
     __syncthreads();
     if (t == 0) {
-        // longest processing time first: each head to the least-loaded queue (ties: lowest);
-        // head_off temporarily holds the head's queue
+        // longest processing time first: each head to the least-loaded queue in use (ties:
+        // lowest); head_off temporarily holds the head's queue
         int64_t qload[kNQ];
         int32_t qlen[kNQ], qstart[kNQ], qrun[kNQ];
         for (int q = 0; q < kNQ; ++q) { qload[q] = 0; qlen[q] = 0; qrun[q] = 0; }
         for (int r = 0; r < nbh; ++r) {
             const int h = horder[r];
             int best = 0;
-            for (int q = 1; q < kNQ; ++q)
+            for (int q = group; q < kNQ; q += group)
                 if (qload[q] < qload[best]) best = q;
             qload[best] += hcost[h];
             qlen[best] += hitems[h];
@@ -126,6 +128,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_global_kernel(
         int32_t sacc = 0;
         for (int h = 0; h < nbh; ++h) { head_slot_base[h] = sacc; sacc += hslots[h]; }
         hdr[kHdrKc] = Kc;
+        hdr[kHdrGroup] = group;
         for (int q = 0; q < kNQ; ++q) {
             hdr[kHdrQStart + q] = qstart[q];
             hdr[kHdrQLen + q] = qlen[q];
@@ -283,6 +286,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_few_kernel(
     }
     if (t == kPlanThreads - 1) {
         hdr[kHdrKc] = Kc;
+        hdr[kHdrGroup] = 1;
         for (int q = 0; q < kNQ; ++q) {
             hdr[kHdrQStart + q] = q == 0 ? 0 : ri;       // the last thread ends at the total
             hdr[kHdrQLen + q] = q == 0 ? ri : 0;
@@ -413,7 +417,7 @@ __global__ __launch_bounds__(2 * B, 2) void attn_kernel(AttnArgs a) {
     const int wv = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform, kept in an SGPR
     const int half = lane >> 5;      // 0 / 1
     const int l32 = lane & 31;
-    const int q0 = xcc_id() % kNQ;
+    const int q0 = (xcc_id() % kNQ) & ~(ld_const(a.hdr, kHdrGroup) - 1);  // first queue
     const int32_t Kc = ld_const(a.hdr, kHdrKc);
 #ifdef BSA_TRACE
     const unsigned long long tr_t0 = __builtin_amdgcn_s_memrealtime();
@@ -733,7 +737,8 @@ bsa_status launch_attn(const void* q_t, const void* k_t, const void* v_t,
     int32_t* hdr = (int32_t*)(w + L.hdr);
     int4* items = (int4*)(w + L.items);
     int32_t* done = (int32_t*)(w + L.done);
-    bsa_status st = launch_plan(row_ptr, batch, heads, D, g, slots, ws, s);
+    // K and V of a head, bf16
+    bsa_status st = launch_plan(row_ptr, batch, heads, D, g, slots, 4 * g.Npad * D, ws, s);
     if (st != BSA_OK) return st;
 
     AttnArgs a;
@@ -761,7 +766,8 @@ bsa_status launch_attn(const void* q_t, const void* k_t, const void* v_t,
 }
 
 bsa_status launch_plan(const int32_t* row_ptr, int32_t batch, int32_t heads, int32_t D,
-                       const Geometry& g, int slots, void* ws, hipStream_t s) {
+                       const Geometry& g, int slots, int64_t head_kv_bytes, void* ws,
+                       hipStream_t s) {
     const AttnLayout L = attn_layout(batch, heads, D, g, slots);
     unsigned char* w = (unsigned char*)ws;
     int32_t* hdr = (int32_t*)(w + L.hdr);
@@ -776,7 +782,8 @@ bsa_status launch_plan(const int32_t* row_ptr, int32_t batch, int32_t heads, int
         return check_launch("plan_few");
     }
     hipLaunchKernelGGL(plan_global_kernel, dim3(1), dim3(kPlanThreads), 0, s, row_ptr, g.n_blk,
-                       nbh, 2 * slots, hdr, head_off, head_slot_base);
+                       nbh, 2 * slots, plan::queue_group(head_kv_bytes), hdr, head_off,
+                       head_slot_base);
     bsa_status st = check_launch("plan_global");
     if (st != BSA_OK) return st;
     hipLaunchKernelGGL(plan_rows_kernel, dim3(nbh), dim3(kPlanThreads), 0, s, row_ptr, g.n_blk,

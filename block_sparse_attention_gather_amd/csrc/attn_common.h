@@ -23,9 +23,10 @@ constexpr float kRescaleThresh = 8.0f;   // log2 units the running max may lag
 
 using AttnLayout = plan::Layout;
 
-// header ints: [0] Kc, [8 .. 8 + kNQ) queue starts, [32 + 32 q] queue counters (128 B apart),
-// [32 + 32 kNQ ..) queue lengths
+// header ints: [0] Kc, [1] XCDs per queue, [8 .. 8 + kNQ) queue starts, [32 + 32 q] queue
+// counters (128 B apart), [32 + 32 kNQ ..) queue lengths
 constexpr int kHdrKc = 0;
+constexpr int kHdrGroup = 1;
 constexpr int kHdrQStart = 8;
 constexpr int kHdrCtr = 32;         // + 32*q
 constexpr int kHdrQLen = 32 + 32 * kNQ;
@@ -155,8 +156,10 @@ __device__ __noinline__ void combine_split(const float* __restrict__ part_o,
 }  // namespace
 
 // Build the persistent schedule of bsa_sparse_attn_fwd for `slots` resident workgroups in the
-// workspace laid out by attn_layout(batch, heads, D, g, slots) (defined with the planner).
+// workspace laid out by attn_layout(batch, heads, D, g, slots) (defined with the planner);
+// head_kv_bytes (K and V of one head as the kernel reads them) sets the queue groups.
 bsa_status launch_plan(const int32_t* row_ptr, int32_t batch, int32_t heads, int32_t D,
-                       const Geometry& g, int slots, void* ws, hipStream_t s);
+                       const Geometry& g, int slots, int64_t head_kv_bytes, void* ws,
+                       hipStream_t s);
 
 }  // namespace bsa

@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnF8Args a) {
     const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
     const int half = lane >> 5;
     const int l32 = lane & 31;
-    const int q0 = xcc_id() % kNQ;
+    const int q0 = (xcc_id() % kNQ) & ~(ld_const(a.hdr, kHdrGroup) - 1);  // first queue
     const int32_t Kc = ld_const(a.hdr, kHdrKc);
     lds_cchar* ks_lds = (lds_cchar*)Ks;
     lds_cchar* vs_lds = (lds_cchar*)Vs;
@@ -429,7 +429,8 @@ bsa_status launch_attn_fp8(const void* q8, const float* qs, const void* k8, cons
     int32_t* hdr = (int32_t*)(w + L.hdr);
     int4* items = (int4*)(w + L.items);
     int32_t* done = (int32_t*)(w + L.done);
-    bsa_status st = launch_plan(row_ptr, batch, heads, 128, g, slots, ws, s);
+    // K and V of a head, E4M3
+    bsa_status st = launch_plan(row_ptr, batch, heads, 128, g, slots, 2 * g.Npad * 128, ws, s);
     if (st != BSA_OK) return st;
     AttnF8Args a;
     a.q = (const uint8_t*)q8;

@@ -10,6 +10,11 @@
 //    blocks, descending, ties by index) and given longest-first to the least-loaded queue, so
 //    a head's K and V stay in one XCD's L2; inside a queue the heads follow in rank order and
 //    each head's rows by cost descending (ties by row), the chunks of a split row consecutive;
+//  * queue groups (head mode): while eight heads' K and V (one head per XCD queue) fit the
+//    memory-side cache in front of HBM (MALL, 256 MiB on MI355X), every XCD has a queue of its
+//    own; past that, pairs of XCDs share one queue (0, 2, 4, 6; the odd ones stay empty), so
+//    four heads are swept at once and the tiles the L2s miss are found in that cache more
+//    often than in HBM;
 //  * few-heads mode (batch * heads < kFewHeads and at most kFewRows rows): whole heads are too
 //    coarse to balance eight queues, so all rows go to queue 0 in one global order, cost
 //    descending (ties by row), and every workgroup takes from it: the last items are the
@@ -32,6 +37,12 @@ constexpr int kNQ = 8;               // XCD queues (MI355X: 8 XCDs)
 constexpr int kMaxHeads = 2048;      // batch * heads supported by the planner
 constexpr int kMaxBlocks = 4096;     // n_blk supported by the planner (12-bit row index)
 constexpr int kKcMin = 8;            // smallest chunk (blocks) a row is split into
+
+// XCDs per queue for heads of `head_kv_bytes` of K and V each (head mode)
+constexpr int64_t kMallBytes = (int64_t)256 << 20;
+BSA_PLAN_FN int32_t queue_group(int64_t head_kv_bytes) {
+    return (int64_t)kNQ * head_kv_bytes > kMallBytes ? 2 : 1;
+}
 
 // chunk size Kc for `total` kept blocks and `target` work items
 BSA_PLAN_FN int32_t chunk_size(int64_t total, int64_t target) {
@@ -84,7 +95,7 @@ struct Layout {
     size_t hdr, head_seg, head_slot_base, items, done, part_o, part_ml, total;
     int64_t max_items, max_slots;
 };
-constexpr int kHdrInts = 32 + 32 * kNQ + kNQ;    // Kc, queue starts, counters, lengths
+constexpr int kHdrInts = 32 + 32 * kNQ + kNQ;    // Kc, group, queue starts, counters, lengths
 BSA_PLAN_FN size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 BSA_PLAN_FN Layout workspace_layout(int64_t bh, int32_t n_blk, int32_t B, int32_t D,
                                     int slots) {

@@ -25,8 +25,10 @@ struct HostPlan {
 };
 
 // Build the schedule of `nbh` heads of n_blk rows each from the CSR row pointers
-// (row_ptr[nbh * n_blk + 1]) for `target` work items (twice the resident workgroups).
-inline HostPlan plan_host(const int32_t* row_ptr, int32_t n_blk, int32_t nbh, int64_t target) {
+// (row_ptr[nbh * n_blk + 1]) for `target` work items (twice the resident workgroups), with
+// `group` XCDs sharing a queue in head mode (queue_group of the head's K and V bytes).
+inline HostPlan plan_host(const int32_t* row_ptr, int32_t n_blk, int32_t nbh, int64_t target,
+                          int32_t group) {
     HostPlan P;
     const int64_t rows = (int64_t)nbh * n_blk;
     P.Kc = chunk_size(row_ptr[rows], target);
@@ -71,12 +73,13 @@ inline HostPlan plan_host(const int32_t* row_ptr, int32_t n_blk, int32_t nbh, in
         for (int q = 1; q < kNQ; ++q) P.qstart[q] = P.qlen[0];
         return P;
     }
-    // head mode: heads longest first to the least-loaded queue (ties: lowest queue)
+    // head mode: heads longest first to the least-loaded queue in use, every group-th (ties:
+    // lowest queue)
     int64_t qload[kNQ] = {};
     std::vector<int32_t> hqueue(nbh);
     for (int32_t r = 0; r < nbh; ++r) {
         int best = 0;
-        for (int q = 1; q < kNQ; ++q)
+        for (int q = group; q < kNQ; q += group)
             if (qload[q] < qload[best]) best = q;
         qload[best] += hcost[order[r]];
         hqueue[order[r]] = best;

@@ -6,11 +6,12 @@
 
 extern "C" {
 
-// Schedule of nbh heads x n_blk rows for `target` work items.  hdr: Kc, qstart[8], qlen[8];
-// head_rank[nbh]; slot_base[nbh]; items[cap][4].  Returns the item count, or -1 if cap is short.
-long long plan_ref(const int* row_ptr, int n_blk, int nbh, long long target, int* hdr,
+// Schedule of nbh heads x n_blk rows for `target` work items, `group` XCDs a queue.  hdr: Kc,
+// qstart[8], qlen[8]; head_rank[nbh]; slot_base[nbh]; items[cap][4].  Returns the item count,
+// or -1 if cap is short.
+long long plan_ref(const int* row_ptr, int n_blk, int nbh, long long target, int group, int* hdr,
                    int* head_rank, int* slot_base, int* items, long long cap) {
-    const bsa::plan::HostPlan P = bsa::plan::plan_host(row_ptr, n_blk, nbh, target);
+    const bsa::plan::HostPlan P = bsa::plan::plan_host(row_ptr, n_blk, nbh, target, group);
     hdr[0] = P.Kc;
     for (int q = 0; q < bsa::plan::kNQ; ++q) {
         hdr[1 + q] = P.qstart[q];
@@ -27,6 +28,9 @@ long long plan_ref(const int* row_ptr, int n_blk, int nbh, long long target, int
     }
     return (long long)P.items.size();
 }
+
+// XCDs per queue for heads of head_kv_bytes of K and V.
+int queue_group_ref(long long head_kv_bytes) { return bsa::plan::queue_group(head_kv_bytes); }
 
 // Workspace offsets: hdr, head_seg, head_slot_base, items, done, part_o, part_ml, total,
 // max_items, max_slots.

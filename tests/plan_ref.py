@@ -23,8 +23,10 @@ def lib():
         L = ctypes.CDLL(out)
         P = ctypes.c_void_p
         L.plan_ref.restype = ctypes.c_longlong
-        L.plan_ref.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_longlong, P, P, P, P,
-                               ctypes.c_longlong]
+        L.plan_ref.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_longlong, ctypes.c_int,
+                               P, P, P, P, ctypes.c_longlong]
+        L.queue_group_ref.restype = ctypes.c_int
+        L.queue_group_ref.argtypes = [ctypes.c_longlong]
         L.layout_ref.restype = None
         L.layout_ref.argtypes = [ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_int, P]
@@ -32,7 +34,12 @@ def lib():
     return _lib
 
 
-def plan(row_ptr, n_blk, nbh, target):
+def queue_group(head_kv_bytes):
+    """XCDs sharing a queue (head mode) for heads of head_kv_bytes of K and V."""
+    return int(lib().queue_group_ref(head_kv_bytes))
+
+
+def plan(row_ptr, n_blk, nbh, target, group=1):
     """-> dict(Kc, qstart, qlen, head_rank, slot_base, items [n, 4] int32)"""
     rp = np.ascontiguousarray(row_ptr, dtype=np.int32)
     assert rp.shape == (nbh * n_blk + 1,)
@@ -41,8 +48,8 @@ def plan(row_ptr, n_blk, nbh, target):
     rank = np.zeros(nbh, np.int32)
     sbase = np.zeros(nbh, np.int32)
     items = np.zeros((cap, 4), np.int32)
-    n = lib().plan_ref(rp.ctypes.data, n_blk, nbh, target, hdr.ctypes.data, rank.ctypes.data,
-                       sbase.ctypes.data, items.ctypes.data, cap)
+    n = lib().plan_ref(rp.ctypes.data, n_blk, nbh, target, group, hdr.ctypes.data,
+                       rank.ctypes.data, sbase.ctypes.data, items.ctypes.data, cap)
     assert n >= 0
     return dict(Kc=int(hdr[0]), qstart=hdr[1:1 + KNQ].copy(), qlen=hdr[1 + KNQ:].copy(),
                 head_rank=rank, slot_base=sbase, items=items[:n].copy())

@@ -2,13 +2,13 @@
 the arithmetic the planner kernels share, plan.h): on ordinary and pathologically skewed row
 lengths, every (row, key block) pair lands in exactly one work item, split rows respect the
 chunk bound and the workspace bounds, the queue layout follows its definition (head mode: heads
-longest-first to the least-loaded XCD queue; few-heads mode: one queue in global cost order),
-and the output is deterministic.  A GPU test checks that the device planner writes this same
+longest-first to the least-loaded XCD queue, or to every other queue when pairs of XCDs share
+one; few-heads mode: one queue in global cost order), and the output is deterministic.  A GPU test checks that the device planner writes this same
 schedule."""
 import numpy as np
 import pytest
 
-from plan_ref import KNQ, plan
+from plan_ref import KNQ, plan, queue_group
 
 pytestmark = pytest.mark.slow
 
@@ -17,10 +17,10 @@ def _row_ptr(costs):
     return np.concatenate([[0], np.cumsum(costs)]).astype(np.int32)
 
 
-def check(costs, n_blk, nbh, target):
+def check(costs, n_blk, nbh, target, group=1):
     costs = np.asarray(costs, np.int64).reshape(nbh * n_blk)
     rp = _row_ptr(costs)
-    P = plan(rp, n_blk, nbh, target)
+    P = plan(rp, n_blk, nbh, target, group)
     nnz = int(costs.sum())
     Kc = max(8, -(-nnz // target))
     assert P["Kc"] == Kc
@@ -71,12 +71,15 @@ def check(costs, n_blk, nbh, target):
         keyv = [(-int(costs[x]), int(x)) for x in seq]
         assert keyv == sorted(keyv)
     else:
-        # head mode: heads longest first to the least-loaded queue; in a queue the heads in
-        # rank order, each head's rows by cost descending (ties by row)
+        # head mode: heads longest first to the least-loaded queue in use (every group-th,
+        # ties: lowest); in a queue the heads in rank order, each head's rows by cost
+        # descending (ties by row)
+        used = np.arange(0, KNQ, group)
+        assert not np.delete(P["qlen"], used).any()
         qload = np.zeros(KNQ, np.int64)
         hq = np.zeros(nbh, np.int64)
         for h in sorted(range(nbh), key=lambda x: (-hc[x], x)):
-            q = int(np.argmin(qload))
+            q = int(used[np.argmin(qload[used])])
             qload[q] += hc[h]
             hq[h] = q
         head = it[:, 0] // n_blk
@@ -90,15 +93,15 @@ def check(costs, n_blk, nbh, target):
             keyv = [(-int(costs[x]), int(x)) for x in sub]
             assert keyv == sorted(keyv)
     # deterministic
-    P2 = plan(rp, n_blk, nbh, target)
+    P2 = plan(rp, n_blk, nbh, target, group)
     assert all(np.array_equal(P[k], P2[k]) for k in P if k != "Kc")
     return P, costs
 
 
-def _queue_rho(P, costs, n_blk):
+def _queue_rho(P, costs, n_blk, group=1):
     it = P["items"]
     loads = [int((it[s:s + n, 2] - it[s:s + n, 1]).sum())
-             for s, n in zip(P["qstart"], P["qlen"])]
+             for s, n in zip(P["qstart"][::group], P["qlen"][::group])]
     return max(loads) / np.mean(loads)
 
 
@@ -188,3 +191,28 @@ def test_rows_without_blocks_are_single_empty_items():
     P, _ = check(costs, 16, 4, 16)
     it = P["items"]
     assert np.sum(it[:, 2] == it[:, 1]) == np.sum(costs == 0)
+
+
+def test_queue_groups_rule():
+    """Pairs of XCDs share a queue once eight heads' K and V (one head a queue) exceed the
+    256 MiB MALL: the bf16 HunyuanVideo-720p and Wan-2.1-720p layers (58 and 37 MiB a head),
+    not Wan-2.1-480p (16 MiB) nor the E4M3 copy of HunyuanVideo-720p (29 MiB)."""
+    kv = lambda n_blk, elem: 2 * n_blk * 128 * 128 * elem
+    assert queue_group(kv(929, 2)) == 2                 # HunyuanVideo-720p, bf16
+    assert queue_group(kv(929, 1)) == 1                 # the same, E4M3
+    assert queue_group(kv(591, 2)) == 2                 # Wan-2.1-720p
+    assert queue_group(kv(256, 2)) == 1                 # Wan-2.1-480p
+    assert queue_group(32 << 20) == 1 and queue_group((32 << 20) + 1) == 2
+
+
+@pytest.mark.parametrize("heads", [16, 24, 40])
+def test_queue_pairs(heads):
+    """Pairs sharing a queue: the heads go longest-first to queues 0, 2, 4 and 6 only, which
+    stay within 5 % of each other; the odd queues are empty."""
+    rng = np.random.default_rng(heads)
+    n = 929
+    dens = rng.permutation(np.linspace(0.2, 0.6, heads))
+    costs = np.stack([np.clip(rng.binomial(n, d, size=n), 8, n) for d in dens])
+    P, c = check(costs, n, heads, 1024, group=2)
+    assert (P["qlen"][0::2] > 0).all() and not P["qlen"][1::2].any()
+    assert _queue_rho(P, c, n, group=2) < 1.05
