@@ -52,6 +52,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_global_kernel(
     __shared__ int32_t hitems[kMaxHeads], hslots[kMaxHeads], horder[kMaxHeads];
     __shared__ uint64_t hkey[kMaxHeads];
     __shared__ int64_t hcost[kMaxHeads];
+    __shared__ uint8_t hq[kMaxHeads];          // queue of the head of each rank
     const int t = threadIdx.x;
     const int64_t rows = (int64_t)nbh * n_blk;
     const int32_t Kc = plan::chunk_size(row_ptr[rows], target);
@@ -104,24 +105,25 @@ __global__ __launch_bounds__(kPlanThreads) void plan_global_kernel(
     __syncthreads();
     if (t == 0) {
         // longest processing time first: each head to the least-loaded queue in use (ties:
-        // lowest); head_off temporarily holds the head's queue
+        // lowest); one thread, so every value it reads back is in registers or LDS
         int64_t qload[kNQ];
         int32_t qlen[kNQ], qstart[kNQ], qrun[kNQ];
         for (int q = 0; q < kNQ; ++q) { qload[q] = 0; qlen[q] = 0; qrun[q] = 0; }
         for (int r = 0; r < nbh; ++r) {
             const int h = horder[r];
             int best = 0;
-            for (int q = group; q < kNQ; q += group)
-                if (qload[q] < qload[best]) best = q;
+#pragma unroll
+            for (int q = 1; q < kNQ; ++q)       // (unrolled: the loads stay in registers)
+                if (q % group == 0 && qload[q] < qload[best]) best = q;
             qload[best] += hcost[h];
             qlen[best] += hitems[h];
-            head_off[h] = best;
+            hq[r] = (uint8_t)best;
         }
         int32_t acc = 0;
         for (int q = 0; q < kNQ; ++q) { qstart[q] = acc; acc += qlen[q]; }
         for (int r = 0; r < nbh; ++r) {
             const int h = horder[r];
-            const int q = head_off[h];
+            const int q = hq[r];
             head_off[h] = qstart[q] + qrun[q];
             qrun[q] += hitems[h];
         }
