@@ -61,7 +61,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_global_kernel(
         for (int h = w; h < nbh; h += kPlanThreads / 64) {
             int32_t ni = 0, ns = 0;
             int64_t hc = 0;
-            for (int i = lane; i < n_blk; i += 64) {
+#pragma unroll 8
+            for (int i = lane; i < n_blk; i += 64) {     // (unrolled: 8 loads in flight)
                 const int64_t r = (int64_t)h * n_blk + i;
                 const int32_t c = row_ptr[r + 1] - row_ptr[r];
                 ni += plan::row_items(c, Kc);
