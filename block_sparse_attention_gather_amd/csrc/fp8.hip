@@ -95,6 +95,15 @@ __device__ __forceinline__ Blk blk_of(const Gather& ga) {
 // 16-byte chunk t mod 16 of that row, read from the tiled tensor or gathered from the raster
 // one (zero past the last real token).  rows: kQB words of LDS for the block's raster rows
 // (written and read here, around a workgroup barrier; RASTER only).
+// 16-byte non-temporal load (raster V is read by the two passes and nothing else: streaming
+// both of them past the caches measured 5-14 % faster than ordinary loads, while streaming only
+// the first, so that the second could find V in the caches, was 4 % slower)
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_nt(const uint4* p) {
+    const nt_u32x4 v = __builtin_nontemporal_load((const nt_u32x4*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <bool RASTER>
 __device__ __forceinline__ void load_block(uint4 (&c)[kPer], const uint4* __restrict__ x,
                                            const Gather& ga, const Blk& k, int t,
@@ -126,7 +135,7 @@ __device__ __forceinline__ void load_block(uint4 (&c)[kPer], const uint4* __rest
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
         const uint32_t r = n[u] != ~0u ? n[u] : 0u;
-        c[u] = x[(((size_t)b * ga.N + r) * ga.heads + h) * (kQD / 8) + dc];
+        c[u] = ld_nt(x + (((size_t)b * ga.N + r) * ga.heads + h) * (kQD / 8) + dc);
     }
 #pragma unroll
     for (int u = 0; u < kPer; ++u)
