@@ -30,6 +30,11 @@ __device__ __forceinline__ void st_nt(uint4* p, const uint4& v) {
     const nt_u32x4 w = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(w, (nt_u32x4*)p);
 }
+typedef unsigned int nt_u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st_nt8(uint2* p, const uint2& v) {
+    const nt_u32x2 w = {v.x, v.y};
+    __builtin_nontemporal_store(w, (nt_u32x2*)p);
+}
 
 // One wavefront per tile position p of batch blockIdx.y moves one token: the heads * D
 // contiguous raster elements <-> `heads` rows of D elements in the tiled layout, as 16-byte
@@ -161,8 +166,8 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_pool_kernel(
         const float inv = amax > 0.f ? 448.0f / amax : 0.f;
 #pragma unroll
         for (int k = 0; k < NP; ++k)
-            x8[((size_t)bh * Npad + lo + rp + RPP * k) * DCH + dc] =
-                amax > 0.f ? codes8(v[k], inv) : make_uint2(0, 0);
+            st_nt8(x8 + ((size_t)bh * Npad + lo + rp + RPP * k) * DCH + dc,
+                   amax > 0.f ? codes8(v[k], inv) : make_uint2(0, 0));
         if (t == 0) x8_scales[(size_t)bh * n_blk + j] = amax / 448.0f;
     }
     if (pooled) {
